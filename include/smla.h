@@ -1,0 +1,159 @@
+/*
+ * smla.h -- C ABI of the sparse MLA attention forward library for AMD MI355X
+ * (gfx950).
+ *
+ * The operation is defined on the page "Ascend Sparse Attention Forward
+ * 算法与优化技术简析", section 数学建模 (mathematical model).  For every query
+ * token t, independently:
+ *
+ *   gathered_kv = KV.index_select(indices[t])        [topk, d_qk]
+ *   P   = Q[t] @ gathered_kv^T                       [h_q, topk]
+ *   S   = softmax(P * sm_scale, dim=-1)              [h_q, topk]
+ *   out = S @ gathered_kv[:, :d_v]                   [h_q, d_v]
+ *   lse = log(sum_j exp(P * sm_scale))               [h_q]   (natural log)
+ *
+ * computed block by block with the online softmax and "skip scale" rule of
+ * the same page, section 计算流程 (computation flow): running maxima and sums in
+ * float32, S cast to bf16 before the product with V, a rescale of the output
+ * accumulator only when some row's running maximum has grown by more than
+ * RESCALE_THRES = 6 since the last rescale.
+ *
+ * Slots: an index outside [0, s_kv) (for example -1) masks its slot: weight
+ * zero, row never read.  Repeated indices are separate slots.  A token (or a
+ * split) with no valid slot yields out = 0 and lse = -inf.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises device memory.
+ *  - Strides are in elements of the tensor's own type unless stated otherwise;
+ *    the innermost dimension is always contiguous.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
+ *    default stream).
+ *  - Every argument is validated on the host before anything is enqueued.  On
+ *    any failure the call returns a non-zero smla_status, enqueues nothing,
+ *    and smla_last_error() describes the cause.  No C++ exception crosses this
+ *    interface; the device code has no error path (bad indices are masked).
+ *  - The library keeps no state between calls; calls on different streams
+ *    with separate outputs and workspaces may run concurrently.
+ */
+#ifndef SMLA_H_
+#define SMLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_ABI_VERSION 1
+
+/* The MLA shapes the kernels are built for: the query/key width d_qk is the
+ * 512-wide latent plus the 64-wide rotary part, and V is the first 512 KV
+ * columns. */
+#define SMLA_D_QK 576
+#define SMLA_D_V 512
+
+/* fp8 KV cache: one float32 scale per group of 128 consecutive columns
+ * (576 columns -> 5 groups, the last 64 wide).  Each token's codes and scales
+ * sit in one 640-byte row, data next to scale (page section
+ * "Decoding KV Cache Layout 优化"): bytes [0, 576) are the E4M3 codes, bytes
+ * [576, 596) the five little-endian float32 scales, bytes [596, 640) padding.
+ * Element value = e4m3(code) * scale[column / 128]. */
+#define SMLA_FP8_GROUP 128
+#define SMLA_FP8_NUM_GROUPS 5
+#define SMLA_FP8_ROW_BYTES 640
+
+/* Largest number of slots one workgroup handles; the planner splits the topk
+ * range of a token into parts no larger than this. */
+#define SMLA_MAX_SLOTS_PER_SPLIT 2048
+
+typedef enum smla_status {
+  SMLA_OK = 0,
+  SMLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride or alignment */
+  SMLA_ERR_UNSUPPORTED = 2,      /* valid request outside the built kernels */
+  SMLA_ERR_WORKSPACE = 3,        /* workspace missing or too small */
+  SMLA_ERR_HIP = 4               /* a HIP runtime call failed */
+} smla_status;
+
+typedef enum smla_kv_format {
+  SMLA_KV_BF16 = 0,    /* kv: bf16 [s_kv, 576], kv_stride_row in elements */
+  SMLA_KV_FP8_E4M3 = 1 /* kv: packed 640-byte rows, kv_stride_row in BYTES */
+} smla_kv_format;
+
+typedef struct smla_fwd_params {
+  /* sizes */
+  int32_t s_q;      /* query tokens, >= 0 */
+  int32_t h_q;      /* query heads: 16, 32, 64 or 128 */
+  int32_t d_qk;     /* must be SMLA_D_QK */
+  int32_t d_v;      /* must be SMLA_D_V */
+  int32_t topk;     /* slots per token, >= 1 */
+  int64_t s_kv;     /* KV rows, 1 .. 2^31-1 */
+  float sm_scale;   /* softmax scale applied to P; finite */
+
+  /* Q: bf16 [s_q, h_q, d_qk]; rows 16-byte aligned */
+  const void* q;
+  int64_t q_stride_token, q_stride_head;
+
+  /* KV: see smla_kv_format; rows 16-byte aligned */
+  const void* kv;
+  int64_t kv_stride_row;
+  int32_t kv_format;
+
+  /* indices: int32 [s_q, topk]; any token stride >= 0 */
+  const int32_t* indices;
+  int64_t indices_stride_token;
+
+  /* out: bf16 [s_q, h_q, d_v] (written); rows 16-byte aligned */
+  void* out;
+  int64_t out_stride_token, out_stride_head;
+
+  /* lse: float32 [s_q, h_q] (written), heads contiguous */
+  float* lse;
+  int64_t lse_stride_token;
+
+  /* tuning: 0 lets the planner choose.
+   *   num_splits: parts of each token's topk range, each run by its own
+   *               workgroup and merged by log-sum-exp (decode occupancy).
+   *   b_topk:     slots per block of the online softmax: 32 or 64. */
+  int32_t num_splits;
+  int32_t b_topk;
+
+  /* Device scratch for split partial results, needed when the plan has more
+   * than one split; size from smla_fwd_workspace_size.  Caller-owned; it may be
+   * reused by later calls on the same stream. */
+  void* workspace;
+  size_t workspace_bytes;
+} smla_fwd_params;
+
+/* The plan the library would run for these parameters (argument checks
+ * included): number of splits and block size. */
+smla_status smla_fwd_plan(const smla_fwd_params* p, int32_t* num_splits, int32_t* b_topk);
+
+/* Bytes of device workspace smla_fwd needs for these parameters (0 when the
+ * plan has a single split). */
+smla_status smla_fwd_workspace_size(const smla_fwd_params* p, size_t* bytes);
+
+/* Enqueue the forward pass: writes out and lse.  Asynchronous on `stream`. */
+smla_status smla_fwd(const smla_fwd_params* p, void* stream);
+
+/* Host helper: pack E4M3 codes [rows, 576] and float32 scales [rows, 5]
+ * (host memory, row-major, contiguous) into 640-byte fp8 KV rows at `packed`
+ * (host memory, rows * 640 bytes, caller-owned).  Padding bytes are zeroed. */
+smla_status smla_pack_fp8_kv_host(const uint8_t* codes, const float* scales, int64_t rows,
+                                  void* packed);
+
+/* Static text for a status code. */
+const char* smla_status_string(int32_t status);
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* smla_last_error(void);
+
+/* SMLA_ABI_VERSION of the loaded library. */
+int32_t smla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H_ */

@@ -1,0 +1,70 @@
+"""Sparse MLA attention forward for AMD MI355X (gfx950).
+
+``sparse_mla_fwd(q, kv, indices, sm_scale) -> (out, lse)`` computes, for every
+query token t independently (page "Ascend Sparse Attention Forward
+算法与优化技术简析", section 数学建模):
+
+    G = kv[indices[t]]                      (slots outside [0, s_kv) are masked)
+    out[t] = softmax(q[t] @ G.T * sm_scale) @ G[:, :512]       bf16 [h_q, 512]
+    lse[t] = logsumexp(q[t] @ G.T * sm_scale)                  fp32 [h_q]
+
+with hand-written HIP kernels behind the C ABI in ``include/smla.h``.  This
+module only marshals tensors; there is no CPU path.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (D_QK, D_V, FP8_ROW_BYTES, SMLA_KV_BF16, SMLA_KV_FP8_E4M3, SmlaError,  # noqa: F401
+                   make_params, smla_fwd, smla_fwd_plan, smla_fwd_workspace_size,
+                   smla_pack_fp8_kv_host)
+
+__all__ = ["sparse_mla_fwd", "pack_fp8_kv", "smla_fwd", "smla_fwd_plan", "smla_fwd_workspace_size",
+           "smla_pack_fp8_kv_host", "SmlaError"]
+
+
+def pack_fp8_kv(codes: torch.Tensor, scales: torch.Tensor, device=None) -> torch.Tensor:
+    """fp8 KV cache in the library's row format (codes and scales of a token
+    side by side, 640 bytes per row), optionally moved to ``device``."""
+    packed = smla_pack_fp8_kv_host(codes.cpu(), scales.cpu())
+    return packed.to(device) if device is not None else packed
+
+
+def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float,
+                   d_v: int = D_V, *, kv_format: str = "bf16", num_splits: int = 0,
+                   b_topk: int = 0, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   stream: int | None = None):
+    """Run the forward pass on the tensors' GPU and return ``(out, lse)``.
+
+    q: bf16 [s_q, h_q, 576]; kv: bf16 [s_kv, 576] or, with ``kv_format="fp8"``,
+    uint8 [s_kv, 640] packed rows (see ``pack_fp8_kv``); indices: int32
+    [s_q, topk].  ``num_splits``/``b_topk`` 0 let the library plan.  Outputs and
+    the split workspace are allocated with torch unless given.
+    """
+    if not q.is_cuda:
+        raise ValueError("sparse_mla_fwd runs on the GPU only: q must be a device tensor")
+    fmt = {"bf16": SMLA_KV_BF16, "fp8": SMLA_KV_FP8_E4M3}[kv_format]
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16")
+    if fmt == SMLA_KV_BF16 and kv.dtype != torch.bfloat16:
+        raise TypeError("bf16 KV must be a bfloat16 tensor")
+    if fmt == SMLA_KV_FP8_E4M3 and kv.dtype != torch.uint8:
+        raise TypeError("fp8 KV must be a uint8 tensor of packed 640-byte rows")
+    if indices.dtype != torch.int32:
+        raise TypeError("indices must be int32")
+    s_q, h_q, _ = q.shape
+    if out is None:
+        out = torch.empty((s_q, h_q, d_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((s_q, h_q), dtype=torch.float32, device=q.device)
+    p = make_params(q, kv, indices, sm_scale, out, lse, kv_format=fmt, num_splits=num_splits,
+                    b_topk=b_topk)
+    need = smla_fwd_workspace_size(p)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    smla_fwd(p, stream)
+    return out, lse

@@ -1,0 +1,227 @@
+// C-ABI layer: argument validation, planning, workspace sizing and launch.
+// Declared in include/smla.h.  Everything here runs on the host; nothing is
+// enqueued unless every check passes.
+#include "smla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "smla_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+smla_status fail(smla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+  int32_t num_splits;
+  int32_t b_topk;
+  int32_t slots_per_split;
+  size_t workspace_bytes;
+};
+
+// Decode occupancy: a token's topk range is cut so that the grid holds at least
+// about two workgroups per CU, with no part smaller than 64 slots and none
+// larger than the LDS index buffer.
+constexpr int kTargetWorkgroups = 512;
+
+smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
+  if (!p) return fail(SMLA_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->d_qk != SMLA_D_QK || p->d_v != SMLA_D_V)
+    return fail(SMLA_ERR_UNSUPPORTED, "d_qk=%d d_v=%d: only d_qk=%d, d_v=%d are built", p->d_qk,
+                p->d_v, SMLA_D_QK, SMLA_D_V);
+  if (p->s_q < 0) return fail(SMLA_ERR_INVALID_ARGUMENT, "s_q=%d is negative", p->s_q);
+  if (p->h_q != 16 && p->h_q != 32 && p->h_q != 64 && p->h_q != 128)
+    return fail(SMLA_ERR_UNSUPPORTED, "h_q=%d: supported 16, 32, 64, 128", p->h_q);
+  if (p->topk < 1) return fail(SMLA_ERR_INVALID_ARGUMENT, "topk=%d must be >= 1", p->topk);
+  if (p->s_kv < 1 || p->s_kv > 2147483647LL)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "s_kv=%lld out of [1, 2^31-1]", (long long)p->s_kv);
+  if (!std::isfinite(p->sm_scale)) return fail(SMLA_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
+  if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_E4M3)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "kv_format=%d unknown", p->kv_format);
+  if (p->b_topk != 0 && p->b_topk != 32 && p->b_topk != 64)
+    return fail(SMLA_ERR_UNSUPPORTED, "b_topk=%d: supported 32, 64 (0 = auto)", p->b_topk);
+  if (p->num_splits < 0) return fail(SMLA_ERR_INVALID_ARGUMENT, "num_splits=%d is negative", p->num_splits);
+
+  if (p->s_q > 0) {
+    if (!p->q || !p->kv || !p->indices || !p->out || !p->lse)
+      return fail(SMLA_ERR_INVALID_ARGUMENT, "a tensor pointer is NULL");
+    if (!aligned16(p->q) || !aligned16(p->kv) || !aligned16(p->out))
+      return fail(SMLA_ERR_INVALID_ARGUMENT, "q, kv and out must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(p->lse) % 4 || reinterpret_cast<uintptr_t>(p->indices) % 4)
+      return fail(SMLA_ERR_INVALID_ARGUMENT, "lse and indices must be 4-byte aligned");
+    // bf16 rows: strides multiples of 8 elements keep every row 16-byte aligned.
+    // Read-only Q may use any token stride (even 0, to broadcast one token).
+    if (p->q_stride_head < SMLA_D_QK || p->q_stride_head % 8 || p->q_stride_token < 0 ||
+        p->q_stride_token % 8)
+      return fail(SMLA_ERR_INVALID_ARGUMENT,
+                  "q strides (token %lld, head %lld): need head >= 576, token >= 0, both multiples "
+                  "of 8", (long long)p->q_stride_token, (long long)p->q_stride_head);
+    if (p->out_stride_head < SMLA_D_V || p->out_stride_head % 8 || p->out_stride_token % 8 ||
+        p->out_stride_token < p->out_stride_head * p->h_q)
+      return fail(SMLA_ERR_INVALID_ARGUMENT,
+                  "out strides (token %lld, head %lld): need head >= 512, token >= h_q*head, both "
+                  "multiples of 8", (long long)p->out_stride_token, (long long)p->out_stride_head);
+    if (p->lse_stride_token < p->h_q)
+      return fail(SMLA_ERR_INVALID_ARGUMENT, "lse_stride_token=%lld < h_q",
+                  (long long)p->lse_stride_token);
+    if (p->indices_stride_token < 0)
+      return fail(SMLA_ERR_INVALID_ARGUMENT, "indices_stride_token=%lld is negative",
+                  (long long)p->indices_stride_token);
+    if (p->kv_format == SMLA_KV_BF16) {
+      if (p->kv_stride_row < SMLA_D_QK || p->kv_stride_row % 8)
+        return fail(SMLA_ERR_INVALID_ARGUMENT,
+                    "kv_stride_row=%lld elements: need >= 576 and a multiple of 8",
+                    (long long)p->kv_stride_row);
+    } else {
+      if (p->kv_stride_row < SMLA_FP8_ROW_BYTES || p->kv_stride_row % 16)
+        return fail(SMLA_ERR_INVALID_ARGUMENT,
+                    "kv_stride_row=%lld bytes: need >= 640 and a multiple of 16",
+                    (long long)p->kv_stride_row);
+      return fail(SMLA_ERR_UNSUPPORTED, "fp8 KV is not built yet");
+    }
+  }
+
+  Plan pl{};
+  pl.b_topk = p->b_topk ? p->b_topk : 64;
+  const int32_t min_splits = (p->topk + SMLA_MAX_SLOTS_PER_SPLIT - 1) / SMLA_MAX_SLOTS_PER_SPLIT;
+  int32_t ns = p->num_splits;
+  if (ns == 0) {
+    ns = min_splits;
+    if (p->s_q > 0 && (int64_t)p->s_q * ns < kTargetWorkgroups) {
+      const int32_t want = (kTargetWorkgroups + p->s_q - 1) / p->s_q;
+      const int32_t cap = (p->topk + 63) / 64;   // parts of at least 64 slots
+      ns = want < cap ? want : cap;
+      if (ns < min_splits) ns = min_splits;
+    }
+  }
+  if (ns < min_splits)
+    return fail(SMLA_ERR_UNSUPPORTED, "num_splits=%d: topk=%d needs at least %d parts of <= %d slots",
+                ns, p->topk, min_splits, SMLA_MAX_SLOTS_PER_SPLIT);
+  if (ns > p->topk) ns = p->topk;
+  pl.num_splits = ns;
+  pl.slots_per_split = (p->topk + ns - 1) / ns;
+  // the parts actually used may be fewer than ns after rounding up
+  pl.num_splits = (p->topk + pl.slots_per_split - 1) / pl.slots_per_split;
+  if ((int64_t)p->s_q * pl.num_splits > 2147483647LL)
+    return fail(SMLA_ERR_UNSUPPORTED, "grid of s_q*num_splits workgroups is too large");
+  pl.workspace_bytes = 0;
+  if (pl.num_splits > 1) {
+    const size_t parts = (size_t)p->s_q * pl.num_splits * p->h_q;
+    pl.workspace_bytes = parts * SMLA_D_V * sizeof(float) + ((parts * sizeof(float) + 255) & ~size_t(255));
+  }
+  *plan = pl;
+  return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status smla_fwd_plan(const smla_fwd_params* p, int32_t* num_splits, int32_t* b_topk) {
+  Plan pl;
+  const smla_status s = check_and_plan(p, &pl);
+  if (s != SMLA_OK) return s;
+  if (num_splits) *num_splits = pl.num_splits;
+  if (b_topk) *b_topk = pl.b_topk;
+  return SMLA_OK;
+}
+
+smla_status smla_fwd_workspace_size(const smla_fwd_params* p, size_t* bytes) {
+  if (!bytes) return fail(SMLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan pl;
+  const smla_status s = check_and_plan(p, &pl);
+  if (s != SMLA_OK) return s;
+  *bytes = pl.workspace_bytes;
+  return SMLA_OK;
+}
+
+smla_status smla_fwd(const smla_fwd_params* p, void* stream) {
+  Plan pl;
+  const smla_status s = check_and_plan(p, &pl);
+  if (s != SMLA_OK) return s;
+  if (p->s_q == 0) return SMLA_OK;
+  if (pl.workspace_bytes) {
+    if (!p->workspace || p->workspace_bytes < pl.workspace_bytes)
+      return fail(SMLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.workspace_bytes,
+                  p->workspace ? p->workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(p->workspace) % 256)
+      return fail(SMLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
+  smla::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(p->q);
+  a.q_st = p->q_stride_token;
+  a.q_sh = p->q_stride_head;
+  a.kv = static_cast<const char*>(p->kv);
+  a.kv_row_bytes = p->kv_format == SMLA_KV_BF16 ? p->kv_stride_row * 2 : p->kv_stride_row;
+  a.idx = p->indices;
+  a.idx_st = p->indices_stride_token;
+  a.out = static_cast<uint16_t*>(p->out);
+  a.out_st = p->out_stride_token;
+  a.out_sh = p->out_stride_head;
+  a.lse = p->lse;
+  a.lse_st = p->lse_stride_token;
+  if (pl.num_splits > 1) {
+    const size_t parts = (size_t)p->s_q * pl.num_splits * p->h_q;
+    a.ws_lse = static_cast<float*>(p->workspace);
+    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
+                                      ((parts * sizeof(float) + 255) & ~size_t(255)));
+  }
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.topk = p->topk;
+  a.slots_per_split = pl.slots_per_split;
+  a.num_splits = pl.num_splits;
+  a.s_kv = p->s_kv;
+  a.scale_log2 = p->sm_scale * 1.4426950408889634f;
+  const hipError_t e = smla::launch_fwd(a, pl.b_topk, p->kv_format == SMLA_KV_FP8_E4M3,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+smla_status smla_pack_fp8_kv_host(const uint8_t* codes, const float* scales, int64_t rows,
+                                  void* packed) {
+  if (rows < 0) return fail(SMLA_ERR_INVALID_ARGUMENT, "rows=%lld is negative", (long long)rows);
+  if (rows > 0 && (!codes || !scales || !packed))
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "a pointer is NULL");
+  char* dst = static_cast<char*>(packed);
+  for (int64_t r = 0; r < rows; ++r) {
+    char* row = dst + r * SMLA_FP8_ROW_BYTES;
+    std::memcpy(row, codes + r * SMLA_D_QK, SMLA_D_QK);
+    std::memcpy(row + SMLA_D_QK, scales + r * SMLA_FP8_NUM_GROUPS, SMLA_FP8_NUM_GROUPS * sizeof(float));
+    std::memset(row + SMLA_D_QK + SMLA_FP8_NUM_GROUPS * sizeof(float), 0,
+                SMLA_FP8_ROW_BYTES - SMLA_D_QK - SMLA_FP8_NUM_GROUPS * sizeof(float));
+  }
+  return SMLA_OK;
+}
+
+const char* smla_status_string(int32_t status) {
+  switch (status) {
+    case SMLA_OK: return "ok";
+    case SMLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SMLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SMLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* smla_last_error(void) { return g_last_error; }
+
+int32_t smla_abi_version(void) { return SMLA_ABI_VERSION; }
+
+}  // extern "C"

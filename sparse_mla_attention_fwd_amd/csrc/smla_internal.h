@@ -1,0 +1,40 @@
+// Internal interface between the C-ABI layer (smla_api.cpp) and the gfx950
+// kernels (smla_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kRowBytesBf16 = kDqk * 2;   // 1152: nine 128-byte lines
+constexpr int kFp8RowBytes = 640;         // 576 codes + 5 float32 scales + pad
+constexpr int kMaxSlotsPerSplit = 2048;
+
+// Everything one launch of the forward kernel needs, by value.
+struct FwdArgs {
+  const uint16_t* q;        // bf16 bits
+  int64_t q_st, q_sh;       // elements
+  const char* kv;           // bf16 rows or packed fp8 rows
+  int64_t kv_row_bytes;     // bytes between consecutive KV rows
+  const int32_t* idx;
+  int64_t idx_st;
+  uint16_t* out;            // bf16 bits
+  int64_t out_st, out_sh;
+  float* lse;
+  int64_t lse_st;
+  float* ws_o;              // [s_q, num_splits, h_q, 512] fp32 (split plans)
+  float* ws_lse;            // [s_q, num_splits, h_q] fp32 (split plans)
+  int32_t s_q, h_q, topk, slots_per_split, num_splits;
+  int64_t s_kv;
+  float scale_log2;         // sm_scale * log2(e)
+};
+
+// Launch the forward pass (and the split combine when num_splits > 1).
+// fp8 selects the packed-fp8 KV producer.  Returns the HIP error of the
+// launches.
+hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,452 @@
+// Sparse MLA attention forward for AMD MI355X (gfx950, CDNA4).
+//
+// Method: page "Ascend Sparse Attention Forward 算法与优化技术简析".
+//   Section 数学建模 (mathematical model): per query token, gather the KV rows
+//   named by the token's indices, P = Q·Gᵀ, S = softmax(P·sm_scale),
+//   out = S·G[:, :d_v].
+//   Section 计算流程 (computation flow): walk the slots in blocks of B_TOPK,
+//   keep running_max, running_max_for_softmax and running_sumexp in fp32,
+//   rescale the output accumulator only when some row's running max exceeds
+//   the max used for the exponentials by more than RESCALE_THRES = 6 ("skip
+//   scale"), cast S to bf16 before the product with V.
+//
+// MI355X design (the page's Ascend Cube/Vector pipeline is prior art only):
+//   * One workgroup per (query token, split of its topk range).  Each wave owns
+//     16 query heads; h_q/16 waves per workgroup.
+//   * Prologue: the split's indices are read once, invalid ones dropped and the
+//     valid ones compacted in order into LDS (masked slots carry zero weight,
+//     so dropping them is exact); only ceil(valid / B_TOPK) blocks run.
+//   * Gather: 16-byte direct-to-LDS loads (global_load_lds_dwordx4), several
+//     blocks in flight in a ring of statically distinct LDS stage buffers.
+//     Rows are stored with a 16-byte-chunk XOR swizzle so that both operand
+//     reads below are free of LDS bank conflicts.
+//   * QKᵀ on MFMA 16x16x32 bf16 as Pᵀ = G·Qᵀ: the key tile is the A operand
+//     read from LDS, Q stays in registers for the whole loop as the B operand.
+//     The result puts one head per lane column and four keys per lane, so row
+//     maxima are in-lane work plus two cross-lane steps.
+//   * Skip-scale decision per wave (its 16 heads), a wave-uniform branch.
+//   * PV as Oᵀ = Vᵀ·Sᵀ: S feeds the B operand straight from registers; the
+//     transposed V operand comes from ds_read_b64_tr_b16 on the same LDS tile;
+//     Oᵀ (fp32, 128 registers per lane) keeps the one-head-per-lane layout, so
+//     a rescale is a per-lane scalar multiply.
+//   * Decode: split-topk partials (normalised output + lse) merged by a
+//     log-sum-exp combine kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smla_internal.h"
+
+namespace smla {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kChunksPerRow = kRowBytesBf16 / 16;   // 72
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// RESCALE_THRES = 6 in natural-log units of the scaled logit; the kernel keeps
+// logits in log2 units (exp2 is the native instruction), so the same test reads
+// running_max - running_max_for_softmax > 6·log2(e).
+constexpr float kRescaleThresLog2 = 6.0f * kLog2e;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// 16-byte chunk c of tile row r lives at chunk position c ^ swz(r).  With the
+// 1152-byte row pitch this makes (a) 16 lanes reading one chunk column of 16
+// consecutive rows and (b) the transposed 8-byte reads of 4 rows x 32 bytes
+// per 16-lane group hit distinct LDS banks.
+__device__ __forceinline__ int swz(int r) { return (r & 6) | ((r >> 3) & 1); }
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * kRowBytesBf16 + ((c ^ swz(r)) << 4);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_load(const char* base, int off) {
+  return *(const LDS_AS T*)((const LDS_AS char*)(const LDS_AS void*)base + off);
+}
+
+// s_waitcnt with vmcnt = vm (clamped to the 6-bit field) and lgkmcnt = 0.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  constexpr int v = VM > 63 ? 63 : VM;
+  __builtin_amdgcn_s_waitcnt((v & 0xF) | ((v >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Workgroup barrier that orders LDS traffic but does not drain outstanding
+// direct-to-LDS gathers (a __syncthreads fence would wait for every one).
+// Callers wait for their own loads first.
+__device__ __forceinline__ void barrier_no_vm_drain() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float wave_max16x4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Compact the valid slots of [lo, hi) of one token's index row into sidx,
+// in order.  Returns the number of valid slots.  All threads participate.
+template <int NW>
+__device__ int compact_slots(const int32_t* __restrict__ irow, int lo, int hi, int64_t s_kv,
+                             int* sidx, int* swcnt, int tid) {
+  constexpr int NT = NW * 64;
+  const int lane = tid & 63, w = tid >> 6;
+  int nvalid = 0;
+  for (int c0 = lo; c0 < hi; c0 += NT) {
+    const int j = c0 + tid;
+    int v = -1;
+    if (j < hi) v = irow[j];
+    const bool ok = (j < hi) && v >= 0 && (int64_t)v < s_kv;
+    const uint64_t m = __ballot(ok);
+    const int pre = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) swcnt[w] = __popcll(m);
+    __syncthreads();
+    int base = nvalid, tot = 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+      const int cnt = swcnt[u];
+      if (u < w) base += cnt;
+      tot += cnt;
+    }
+    if (ok) sidx[base + pre] = v;
+    nvalid += tot;
+    __syncthreads();
+  }
+  return nvalid;
+}
+
+// Enqueue the gather of one block (BT compacted slots) into an LDS stage.
+// Slot positions are contiguous per wave instruction (direct-to-LDS writes go
+// to M0 + 16·lane); each lane fetches the global chunk whose swizzled position
+// is its slot.  Padding slots past the valid count hold the token's first
+// valid row: it is finite, and the softmax gives those slots weight exactly 0.
+template <int NW, int BT>
+__device__ __forceinline__ void issue_gather_bf16(char* stage, const char* __restrict__ kv,
+                                                  int64_t row_bytes, const int* sidx_blk, int tid) {
+  constexpr int NT = NW * 64;
+  constexpr int CH = BT * kChunksPerRow;
+  constexpr int LPB = (CH + NT - 1) / NT;
+  const int w = tid >> 6;
+#pragma unroll
+  for (int k = 0; k < LPB; ++k) {
+    const int slot = k * NT + tid;
+    if (CH % NT == 0 || slot < CH) {
+      const int row = slot / kChunksPerRow;
+      const int pos = slot - row * kChunksPerRow;
+      const int c = pos ^ swz(row);
+      const char* src = kv + (int64_t)sidx_blk[row] * row_bytes + (c << 4);
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (LDS_AS void*)(stage + (k * NT + w * 64) * 16), 16, 0, 0);
+    }
+  }
+}
+
+template <int NW, int BT>
+constexpr int loads_per_block() {
+  return (BT * kChunksPerRow + NW * 64 - 1) / (NW * 64);
+}
+
+// Wait until at most `pend` later blocks' gathers are outstanding, plus all
+// LDS traffic.  pend is in [0, NST-2].
+template <int LPB, int NST>
+__device__ __forceinline__ void wait_block(int pend) {
+  if constexpr (NST > 3) {
+    if (pend >= 2) { wait_vm_lgkm0<2 * LPB>(); return; }
+  }
+  if constexpr (NST > 2) {
+    if (pend >= 1) { wait_vm_lgkm0<LPB>(); return; }
+  }
+  wait_vm_lgkm0<0>();
+}
+
+// Per-wave online-softmax state for 16 heads (one per lane column).
+struct State {
+  f32x4 o[32];      // Oᵀ[dv = 16·dt + 4·g + r][head n]
+  float running_max;
+  float running_max_for_softmax;
+  float sumexp;     // this lane's partial running_sumexp (keys 4g..4g+3 of each tile)
+};
+
+// Per-lane LDS byte offsets of the two operand reads.  The chunk swizzle only
+// flips the low three bits of a chunk index, so every step of the unrolled
+// loops adds a compile-time immediate to one of a few per-lane bases.
+struct LaneOffsets {
+  int qk[2];   // K operand, chunk 4s+g of row n: s even / odd
+  int tr[4];   // V operand, row 4g + n/4, chunk 2dt + ((n&3)>>1): dt mod 4
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+  const int g = lane >> 4, n = lane & 15;
+  LaneOffsets o;
+#pragma unroll
+  for (int v = 0; v < 2; ++v) o.qk[v] = n * kRowBytesBf16 + (((4 * v + g) ^ swz(n)) << 4);
+  const int row = 4 * g + (n >> 2);
+  const int cadd = (n & 3) >> 1;
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    o.tr[v] = row * kRowBytesBf16 + (((2 * v + cadd) ^ swz(row)) << 4) + (n & 1) * 8;
+  return o;
+}
+
+// One block: QKᵀ, skip-scale online softmax, PV.
+template <int BT>
+__device__ __forceinline__ void compute_block(const char* tile, const LaneOffsets& lo,
+                                              const bf16x8 (&qf)[18], State& st,
+                                              int blk, int nvalid, float scale_log2, int lane) {
+  constexpr int KT = BT / 16;
+  const int g = lane >> 4;
+  // Pᵀ = G·Qᵀ over d_qk = 576 = 18 steps of 32.  Row 16kt + n has the same
+  // swizzle as row n; chunk 4s + g = 8(s/2) + (4(s&1) + g).
+  f32x4 p[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) p[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 18; ++s) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const bf16x8 a = lds_load<bf16x8>(tile, lo.qk[s & 1] + kt * 16 * kRowBytesBf16 + (s >> 1) * 128);
+      p[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], p[kt], 0, 0, 0);
+    }
+  }
+  // Scaled logits in log2 units; slots past the compacted count are masked.
+  float x[KT][4];
+  float cur = kNegInf;
+  const int j0 = blk * BT + 4 * g;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = p[kt][r] * scale_log2;
+      x[kt][r] = (j0 + 16 * kt + r < nvalid) ? v : kNegInf;
+      cur = fmaxf(cur, x[kt][r]);
+    }
+  }
+  cur = wave_max16x4(cur);
+  // Every block holds at least one valid slot, so the new running max is finite.
+  const float rmax = fmaxf(st.running_max, cur);
+  st.running_max = rmax;
+  const bool trig = rmax - st.running_max_for_softmax > kRescaleThresLog2;
+  if (__ballot(trig) != 0ull) {
+    // exp2(-inf) = 0 on the first block: the zero state stays zero.
+    const float alpha = __builtin_amdgcn_exp2f(st.running_max_for_softmax - rmax);
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) st.o[dt] *= alpha;
+    st.sumexp *= alpha;
+    st.running_max_for_softmax = rmax;
+  }
+  const float m = st.running_max_for_softmax;
+  float sv[KT][4];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[kt][r] = __builtin_amdgcn_exp2f(x[kt][r] - m);
+      st.sumexp += sv[kt][r];
+    }
+  }
+  // Oᵀ += Vᵀ·Sᵀ, 32 keys per MFMA step.  Lane (g, n) holds S for head n and
+  // keys {32ks + 4g + e, 32ks + 16 + 4g + e}, e < 4; the transposed reads give
+  // the V operand the same key order.
+#pragma unroll
+  for (int ks = 0; ks < BT / 32; ++ks) {
+    union { uint32_t u[4]; bf16x8 v; } sb;
+    sb.u[0] = pack2_bf16(sv[2 * ks][0], sv[2 * ks][1]);
+    sb.u[1] = pack2_bf16(sv[2 * ks][2], sv[2 * ks][3]);
+    sb.u[2] = pack2_bf16(sv[2 * ks + 1][0], sv[2 * ks + 1][1]);
+    sb.u[3] = pack2_bf16(sv[2 * ks + 1][2], sv[2 * ks + 1][3]);
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      // rows 32ks + 4g + n/4 and 16 rows further; chunk 2dt + .. = 8(dt/4) + ..
+      const int off = lo.tr[dt & 3] + 32 * ks * kRowBytesBf16 + (dt >> 2) * 128;
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off));
+      const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off + 16 * kRowBytesBf16));
+      union { i16x4 h[2]; bf16x8 v; } a;
+      a.h[0] = va;
+      a.h[1] = vb;
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, sb.v, st.o[dt], 0, 0, 0);
+    }
+  }
+}
+
+template <int NW, int BT, int NST, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int LPB = loads_per_block<NW, BT>();
+  constexpr int TILE = BT * kRowBytesBf16;
+  // Statically distinct stage buffers: the compiler tracks direct-to-LDS
+  // writes per LDS object, so reading one stage never waits for the gathers
+  // still in flight into the others.
+  __shared__ __attribute__((aligned(1024))) char st0[TILE];
+  __shared__ __attribute__((aligned(1024))) char st1[TILE];
+  __shared__ __attribute__((aligned(16))) char st2[NST > 2 ? TILE : 16];
+  __shared__ __attribute__((aligned(16))) char st3[NST > 3 ? TILE : 16];
+  __shared__ int sidx[kMaxSlotsPerSplit + BT];
+  __shared__ int swcnt[NW];
+  char* const stages[4] = {st0, st1, st2, st3};
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int token = blockIdx.x / a.num_splits;
+  const int split = blockIdx.x - token * a.num_splits;
+  const int lo = split * a.slots_per_split;
+  const int hi = min(a.topk, lo + a.slots_per_split);
+
+  const int nvalid = compact_slots<NW>(a.idx + (int64_t)token * a.idx_st, lo, hi, a.s_kv, sidx,
+                                       swcnt, tid);
+  const int nblk = (nvalid + BT - 1) / BT;
+  // Padding slots of the last block repeat the first valid row (weight 0).
+  for (int j = nvalid + tid; j < nblk * BT; j += NW * 64) sidx[j] = sidx[0];
+  __syncthreads();
+
+  // Q for this wave's 16 heads: B operand of Pᵀ = G·Qᵀ, lane (g, n) holds
+  // Q[head n][32s + 8g .. 32s + 8g + 7].
+  const int head = w * 16 + n;
+  bf16x8 qf[18];
+  {
+    const uint16_t* qrow = a.q + (int64_t)token * a.q_st + (int64_t)head * a.q_sh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qf[s] = *(const bf16x8*)(qrow + 32 * s);
+  }
+
+  State st;
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.running_max = kNegInf;
+  st.running_max_for_softmax = kNegInf;
+  st.sumexp = 0.f;
+
+  const LaneOffsets lofs = lane_offsets(lane);
+
+  // Prologue: NST-1 blocks in flight.
+#pragma unroll
+  for (int b = 0; b < NST - 1; ++b)
+    if (b < nblk) issue_gather_bf16<NW, BT>(stages[b], a.kv, a.kv_row_bytes, sidx + b * BT, tid);
+
+  for (int i0 = 0; i0 < nblk; i0 += NST) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      const int i = i0 + s;
+      if (i < nblk) {
+        wait_block<LPB, NST>(min(nblk - 1, i + NST - 2) - i);
+        barrier_no_vm_drain();
+        if (i + NST - 1 < nblk)
+          issue_gather_bf16<NW, BT>(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes,
+                                    sidx + (i + NST - 1) * BT, tid);
+        compute_block<BT>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane);
+      }
+    }
+  }
+
+  // Epilogue: total running_sumexp per head, normalise, write.
+  float l = st.sumexp;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const bool empty = nvalid == 0;
+  const float inv = empty ? 0.f : 1.0f / l;
+  const float lse = empty ? kNegInf : (st.running_max_for_softmax + __builtin_amdgcn_logf(l)) * kLn2;
+  if constexpr (!SPLIT) {
+    uint16_t* orow = a.out + (int64_t)token * a.out_st + (int64_t)head * a.out_sh + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      i32x2 v;
+      v[0] = (int)pack2_bf16(st.o[dt][0] * inv, st.o[dt][1] * inv);
+      v[1] = (int)pack2_bf16(st.o[dt][2] * inv, st.o[dt][3] * inv);
+      *(i32x2*)(orow + 16 * dt) = v;
+    }
+    if (g == 0) a.lse[(int64_t)token * a.lse_st + head] = lse;
+  } else {
+    const int64_t part = ((int64_t)token * a.num_splits + split) * a.h_q + head;
+    float* orow = a.ws_o + part * kDv + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) *(f32x4*)(orow + 16 * dt) = st.o[dt] * inv;
+    if (g == 0) a.ws_lse[part] = lse;
+  }
+}
+
+// Log-sum-exp merge of split partials: one thread per (token, head, 8 columns).
+__global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.s_q * a.h_q * (kDv / 8);
+  if (t >= total) return;
+  const int q8 = (int)(t % (kDv / 8));
+  const int64_t th = t / (kDv / 8);
+  const int head = (int)(th % a.h_q);
+  const int64_t token = th / a.h_q;
+  const int ns = a.num_splits;
+  const int64_t part0 = token * ns * a.h_q + head;
+  float m = kNegInf;
+  for (int s = 0; s < ns; ++s) m = fmaxf(m, a.ws_lse[part0 + (int64_t)s * a.h_q]);
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  float z = 0.f;
+  if (m != kNegInf) {
+    for (int s = 0; s < ns; ++s) {
+      const int64_t part = part0 + (int64_t)s * a.h_q;
+      const float ls = a.ws_lse[part];
+      if (ls == kNegInf) continue;
+      const float wgt = __expf(ls - m);
+      z += wgt;
+      const f32x4* src = (const f32x4*)(a.ws_o + part * kDv + 8 * q8);
+      acc0 += wgt * src[0];
+      acc1 += wgt * src[1];
+    }
+  }
+  const float inv = z > 0.f ? 1.0f / z : 0.f;
+  i32x4 v;
+  v[0] = (int)pack2_bf16(acc0[0] * inv, acc0[1] * inv);
+  v[1] = (int)pack2_bf16(acc0[2] * inv, acc0[3] * inv);
+  v[2] = (int)pack2_bf16(acc1[0] * inv, acc1[1] * inv);
+  v[3] = (int)pack2_bf16(acc1[2] * inv, acc1[3] * inv);
+  *(i32x4*)(a.out + token * a.out_st + (int64_t)head * a.out_sh + 8 * q8) = v;
+  if (q8 == 0) a.lse[token * a.lse_st + head] = z > 0.f ? m + __logf(z) : kNegInf;
+}
+
+template <int NW, int BT, bool SPLIT>
+hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
+  constexpr int NST = BT == 32 ? 4 : 2;
+  const unsigned grid = (unsigned)((int64_t)a.s_q * a.num_splits);
+  hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT>), dim3(grid), dim3(NW * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_nw(const FwdArgs& a, int b_topk, hipStream_t stream) {
+  const bool split = a.num_splits > 1;
+  if (b_topk == 64) return split ? launch_bf16<NW, 64, true>(a, stream) : launch_bf16<NW, 64, false>(a, stream);
+  return split ? launch_bf16<NW, 32, true>(a, stream) : launch_bf16<NW, 32, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream) {
+  if (fp8) return hipErrorNotSupported;
+  hipError_t e;
+  switch (a.h_q) {
+    case 16: e = launch_nw<1>(a, b_topk, stream); break;
+    case 32: e = launch_nw<2>(a, b_topk, stream); break;
+    case 64: e = launch_nw<4>(a, b_topk, stream); break;
+    case 128: e = launch_nw<8>(a, b_topk, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess || a.num_splits <= 1) return e;
+  const int64_t threads = (int64_t)a.s_q * a.h_q * (kDv / 8);
+  hipLaunchKernelGGL(smla_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/smla.h declares, validates arguments on the host (returning a status
+and enqueuing nothing) and plans the named workloads as documented."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_mla_attention_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(smla_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(declared) == sorted(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.smla_abi_version() == 1
+
+
+def test_params_struct_layout_matches_header(tmp_path):
+    """Every field offset of the ctypes mirror equals the C compiler's."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler to read the header's layout")
+    fields = [f for f, _ in _lib.smla_fwd_params._fields_]
+    src = tmp_path / "off.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "smla.h"\nint main(void){\n'
+                   + f'printf("%zu\\n", sizeof(smla_fwd_params));\n'
+                   + "".join(f'printf("%zu\\n", offsetof(smla_fwd_params, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "off"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    P = _lib.smla_fwd_params
+    assert got[0] == ctypes.sizeof(P)
+    assert got[1:] == [getattr(P, f).offset for f in fields]
+
+
+FAKE = 1 << 20   # 16-byte aligned fake device addresses: never dereferenced on failure paths
+
+
+def _params(**kw):
+    p = _lib.smla_fwd_params()
+    p.s_q, p.h_q, p.d_qk, p.d_v, p.topk, p.s_kv = 4, 16, 576, 512, 128, 2048
+    p.sm_scale = 1 / 24
+    p.q, p.q_stride_token, p.q_stride_head = FAKE, 16 * 576, 576
+    p.kv, p.kv_stride_row, p.kv_format = FAKE * 2, 576, 0
+    p.indices, p.indices_stride_token = FAKE * 3, 128
+    p.out, p.out_stride_token, p.out_stride_head = FAKE * 4, 16 * 512, 512
+    p.lse, p.lse_stride_token = FAKE * 5, 16
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d_qk", 512, _lib.SMLA_ERR_UNSUPPORTED),
+    ("d_v", 576, _lib.SMLA_ERR_UNSUPPORTED),
+    ("h_q", 24, _lib.SMLA_ERR_UNSUPPORTED),
+    ("h_q", 256, _lib.SMLA_ERR_UNSUPPORTED),
+    ("s_q", -1, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("topk", 0, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("s_kv", 0, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("s_kv", 1 << 31, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("sm_scale", float("nan"), _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("q", 0, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("lse", 0, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("q", FAKE + 8, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("q_stride_head", 575, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("kv_stride_row", 580, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("out_stride_token", 512, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("lse_stride_token", 8, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("kv_format", 7, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("b_topk", 48, _lib.SMLA_ERR_UNSUPPORTED),
+    ("num_splits", -2, _lib.SMLA_ERR_INVALID_ARGUMENT),
+])
+def test_invalid_arguments_are_rejected_on_the_host(field, value, status):
+    lib = _lib.load()
+    p = _params(**{field: value})
+    # smla_fwd would enqueue work on success; every case here fails validation
+    # first, so no HIP call is made and no GPU is needed.
+    assert lib.smla_fwd(ctypes.byref(p), None) == status
+    assert _lib.last_error() != ""
+    n = ctypes.c_size_t(123)
+    assert lib.smla_fwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+
+
+def test_null_params_and_status_strings():
+    lib = _lib.load()
+    assert lib.smla_fwd(None, None) == _lib.SMLA_ERR_INVALID_ARGUMENT
+    for s in range(5):
+        assert lib.smla_status_string(s).decode()
+    assert lib.smla_status_string(99).decode() == "unknown status"
+
+
+def test_empty_batch_is_a_no_op():
+    lib = _lib.load()
+    p = _params(s_q=0, q=0, kv=0, indices=0, out=0, lse=0)
+    assert lib.smla_fwd(ctypes.byref(p), None) == _lib.SMLA_OK
+
+
+def test_workspace_required_for_split_plans():
+    lib = _lib.load()
+    p = _params(num_splits=3)
+    assert _lib.smla_fwd_plan(p) == (3, 64)
+    need = _lib.smla_fwd_workspace_size(p)
+    parts = 4 * 3 * 16
+    assert need == parts * 512 * 4 + ((parts * 4 + 255) // 256) * 256
+    assert lib.smla_fwd(ctypes.byref(p), None) == _lib.SMLA_ERR_WORKSPACE
+    p.workspace, p.workspace_bytes = FAKE * 6, need - 1
+    assert lib.smla_fwd(ctypes.byref(p), None) == _lib.SMLA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("name,splits", [("tiny", None), ("prefill", 1), ("causal", 1), ("decode", 4)])
+def test_plans_of_named_workloads(name, splits):
+    import workloads
+    w = workloads.WORKLOADS[name]
+    p = _params(s_q=w.s_q, h_q=w.h_q, topk=w.topk, s_kv=w.s_kv, num_splits=w.num_splits,
+                q_stride_token=w.h_q * 576, out_stride_token=w.h_q * 512, lse_stride_token=w.h_q,
+                indices_stride_token=w.topk)
+    ns, bt = _lib.smla_fwd_plan(p)
+    if splits is not None:
+        assert ns == splits
+    assert bt in (32, 64)
+    assert (w.topk + ns - 1) // ns <= _lib.MAX_SLOTS_PER_SPLIT
+
+
+def test_topk_beyond_one_split_needs_more_parts():
+    p = _params(topk=5000, indices_stride_token=5000, num_splits=2)
+    with pytest.raises(_lib.SmlaError):
+        _lib.smla_fwd_plan(p)
+    p.num_splits = 0
+    ns, _ = _lib.smla_fwd_plan(p)
+    assert ns >= 3
+
+
+def test_pack_fp8_rows_host():
+    rng = np.random.default_rng(0)
+    codes = torch.from_numpy(rng.integers(0, 256, (7, 576), dtype=np.uint8))
+    scales = torch.from_numpy(rng.random((7, 5), dtype=np.float32))
+    packed = _lib.smla_pack_fp8_kv_host(codes, scales)
+    assert packed.shape == (7, 640)
+    assert torch.equal(packed[:, :576], codes)
+    assert torch.equal(packed[:, 576:596].contiguous().view(torch.float32), scales)
+    assert torch.all(packed[:, 596:] == 0)

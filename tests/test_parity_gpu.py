@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bar: out max-abs error <= 2e-2 * max|out_ref| over the case, lse within 1e-3
+absolute, and -inf exactly where the oracle has -inf (tokens without a valid
+slot).  Index handling and masking are checked bit-exactly where the result
+has a unique bf16 value (all slots on one row; poisoned unreferenced rows).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import dequant_fp8_rows, sparse_mla_fwd_exact
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_mla_attention_fwd_amd as smla  # loads libsmla.so; fails loudly if absent
+    return torch.device("cuda:0"), smla
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def oracle_tokens(x, tokens=None):
+    """Run the oracle on a subset of tokens, gathering only the KV rows they
+    reference (indices are remapped; masked slots stay masked)."""
+    idx = x["indices"].numpy()
+    q = x["q"]
+    if tokens is not None:
+        idx = idx[tokens]
+        q = q[tokens]
+    s_kv = x["kv"].shape[0] if "kv" in x else x["kv_codes"].shape[0]
+    valid = (idx >= 0) & (idx < s_kv)
+    rows = np.unique(idx[valid])
+    remap = np.full(idx.shape, -1, dtype=np.int64)
+    remap[valid] = np.searchsorted(rows, idx[valid])
+    if "kv" in x:
+        kv = workloads.to_f64(x["kv"][torch.from_numpy(rows)]) if rows.size else np.zeros((1, 576))
+    else:
+        kv = dequant_fp8_rows(x["kv_codes"][torch.from_numpy(rows)].numpy(),
+                              x["kv_scales"][torch.from_numpy(rows)].numpy()) if rows.size else np.zeros((1, 576))
+    return sparse_mla_fwd_exact(workloads.to_f64(q), kv, remap, x["sm_scale"], 512)
+
+
+def run_gpu(dev, x, **kw):
+    device, smla = dev
+    q = x["q"].to(device)
+    idx = x["indices"].to(device)
+    if "kv" in x:
+        kv = x["kv"].to(device)
+        out, lse = smla.sparse_mla_fwd(q, kv, idx, x["sm_scale"], **kw)
+    else:
+        kv = smla.pack_fp8_kv(x["kv_codes"], x["kv_scales"], device)
+        out, lse = smla.sparse_mla_fwd(q, kv, idx, x["sm_scale"], kv_format="fp8", **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64)
+
+
+def check(out, lse, ro, rl, what=""):
+    assert np.isfinite(out).all(), f"{what}: non-finite output"
+    neg = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), neg), f"{what}: -inf lse mismatch"
+    assert np.all(out[neg] == 0), f"{what}: empty rows must be zero"
+    scale = max(np.abs(ro).max(), 1e-30)
+    err = np.abs(out - ro).max()
+    lerr = np.abs(lse[~neg] - rl[~neg]).max() if (~neg).any() else 0.0
+    _say(f"  {what}: out err {err:.3e} (tol {OUT_TOL * scale:.3e}), lse err {lerr:.3e}")
+    assert err <= OUT_TOL * scale, f"{what}: out error {err} > {OUT_TOL} * {scale}"
+    assert lerr <= LSE_TOL, f"{what}: lse error {lerr}"
+    return err / scale, lerr
+
+
+def test_tiny_workload_all_tokens(dev):
+    x = workloads.make_inputs("tiny")
+    out, lse = run_gpu(dev, x)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, "tiny")
+
+
+@pytest.mark.parametrize("h_q", [16, 32, 64, 128])
+@pytest.mark.parametrize("b_topk", [32, 64])
+def test_random_cases_heads_and_blocks(dev, h_q, b_topk):
+    # topk 257: several blocks plus a ragged tail of one slot
+    x = workloads.make_random(s_q=3, h_q=h_q, topk=257, s_kv=1000, seed=h_q + b_topk)
+    out, lse = run_gpu(dev, x, b_topk=b_topk, num_splits=1)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"h{h_q} B{b_topk}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 0])
+def test_splits_and_combine(dev, num_splits):
+    x = workloads.make_random(s_q=5, h_q=64, topk=300, s_kv=4096, seed=40 + num_splits,
+                              invalid_frac=0.3)
+    x["indices"][1, :] = -1                  # token 1: every split empty
+    x["indices"][2, :200] = -1               # token 2: the first splits empty
+    out, lse = run_gpu(dev, x, num_splits=num_splits)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"splits={num_splits}")
+
+
+def test_masking_duplicates_and_ragged(dev):
+    x = workloads.make_random(s_q=6, h_q=64, topk=130, s_kv=777, seed=7, invalid_frac=0.25,
+                              dup_frac=0.2, q_mult=4.0)
+    idx = x["indices"]
+    idx[0, :] = -1                           # no valid slot at all
+    idx[1, :129] = -1                        # only the last slot valid
+    idx[2, 1:] = 10 ** 6                     # only the first slot valid (rest past s_kv)
+    out, lse = run_gpu(dev, x)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, "masking")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+@pytest.mark.parametrize("topk", [1, 2, 31, 33, 64, 65, 2048])
+def test_topk_edges(dev, topk):
+    x = workloads.make_random(s_q=2, h_q=64, topk=topk, s_kv=3000, seed=topk)
+    out, lse = run_gpu(dev, x)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"topk={topk}")
+
+
+@pytest.mark.parametrize("k", [1, 64, 2048])
+def test_all_slots_one_row_is_bit_exact(dev, k):
+    """Every slot names row r: all logits are equal, S = 1 exactly, the sum is
+    exact in fp32 and out/l rounds back to the bf16 row itself."""
+    x = workloads.make_random(s_q=3, h_q=64, topk=k, s_kv=500, seed=k)
+    rows = [5, 499, 0]
+    for t, r in enumerate(rows):
+        x["indices"][t, :] = r
+    for ns in (1, 4) if k >= 4 else (1,):
+        out, lse = run_gpu(dev, x, num_splits=ns)
+        for t, r in enumerate(rows):
+            v = x["kv"][r, :512].float().numpy()
+            assert np.array_equal(out[t], np.broadcast_to(v, out[t].shape)), f"row {r} not exact"
+            xr = (workloads.to_f64(x["q"][t]) @ workloads.to_f64(x["kv"][r])) * x["sm_scale"]
+            assert np.abs(lse[t] - (xr + math.log(k))).max() < 1e-4
+
+
+def test_unreferenced_rows_are_never_read(dev):
+    """Rows no valid slot names are NaN; any read of them would leak a NaN."""
+    x = workloads.make_random(s_q=8, h_q=64, topk=200, s_kv=2048, seed=3, invalid_frac=0.3)
+    idx = x["indices"].numpy()
+    used = np.zeros(2048, dtype=bool)
+    used[idx[(idx >= 0) & (idx < 2048)]] = True
+    kv = x["kv"].clone()
+    kv[torch.from_numpy(~used)] = float("nan")
+    x2 = dict(x, kv=kv)
+    out, lse = run_gpu(dev, x2)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, "poisoned")
+
+
+def test_deterministic(dev):
+    x = workloads.make_random(s_q=16, h_q=64, topk=512, s_kv=8192, seed=11, q_mult=4.0)
+    a = run_gpu(dev, x)
+    for _ in range(3):
+        b = run_gpu(dev, x)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_block_sizes_agree(dev):
+    x = workloads.make_random(s_q=4, h_q=64, topk=1000, s_kv=8192, seed=12, q_mult=4.0)
+    a = run_gpu(dev, x, b_topk=32)
+    b = run_gpu(dev, x, b_topk=64)
+    ro, rl = oracle_tokens(x)
+    check(*a, ro, rl, "B32")
+    check(*b, ro, rl, "B64")
+
+
+def test_strided_views(dev):
+    """Non-default strides: Q and out as head-sliced views, KV rows padded."""
+    device, smla = dev
+    x = workloads.make_random(s_q=3, h_q=16, topk=100, s_kv=300, seed=5)
+    qbig = torch.zeros((3, 24, 576 + 64), dtype=torch.bfloat16)
+    qbig[:, 4:20, :576] = x["q"]
+    kvbig = torch.zeros((300, 576 + 128), dtype=torch.bfloat16)
+    kvbig[:, :576] = x["kv"]
+    q = qbig.to(device)[:, 4:20, :576]
+    kv = kvbig.to(device)[:, :576]
+    idx = torch.zeros((3, 136), dtype=torch.int32)
+    idx[:, :100] = x["indices"]
+    idx = idx.to(device)[:, :100]
+    outbig = torch.full((3, 20, 520), 7.0, dtype=torch.bfloat16, device=device)
+    out = outbig[:, 2:18, :512]
+    lsebig = torch.full((3, 40), 7.0, dtype=torch.float32, device=device)
+    lse = lsebig[:, 8:24]
+    smla.sparse_mla_fwd(q, kv, idx, x["sm_scale"], out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle_tokens(x)
+    check(out.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64), ro, rl, "strided")
+    ob = outbig.cpu()
+    assert torch.all(ob[:, :2] == 7) and torch.all(ob[:, 18:] == 7) and torch.all(ob[:, :, 512:] == 7)
+    lb = lsebig.cpu()
+    assert torch.all(lb[:, :8] == 7) and torch.all(lb[:, 24:] == 7)
+
+
+# ---- full-size workloads: the launch the benchmark times, checked on sampled tokens
+
+
+def _sampled(dev, x, tokens, **kw):
+    out, lse = run_gpu(dev, x, **kw)
+    ro, rl = oracle_tokens(x, tokens)
+    return check(out[tokens], lse[tokens], ro, rl, f"{x['workload'].name} sampled")
+
+
+def test_prefill_full_size_sampled(dev):
+    x = workloads.make_inputs("prefill")
+    tokens = np.array([0, 1, 777, 2048, 4094, 4095])
+    _sampled(dev, x, tokens)
+
+
+def test_causal_full_size_sampled(dev):
+    x = workloads.make_inputs("causal")
+    tokens = np.array([0, 1, 2, 31, 32, 33, 63, 64, 65, 2046, 2047, 2048, 5000, 8191])
+    _sampled(dev, x, tokens)
+
+
+def test_decode_full_size_all_tokens(dev):
+    x = workloads.make_inputs("decode")
+    _sampled(dev, x, np.arange(64), num_splits=4)
