@@ -1,0 +1,192 @@
+"""Benchmark of the sparse MLA attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+A step is one forward pass over the whole workload (every token, every
+head): one call of the library's entry point, which launches the fused
+kernel (plus the split combine for decode plans).  Inputs are resident in HBM
+before the timed region; K steps run back to back between two device
+synchronisations.  Prints one JSON line.
+
+Default workload: prefill, 4096 query tokens, h_q 64, topk 2048, d_qk 576,
+d_v 512, one shared bf16 KV of 65536 rows, indices uniform without
+replacement per token.
+
+``roofline``: algorithmic FLOPs of one launch (2·h_q·(d_qk + d_v) per valid
+slot) over the average launch duration, measured with HIP events recorded on
+the stream the kernel runs on, against the MI355X dense bf16 MFMA peak.
+``cpu_baseline``: the float64 CPU oracle timed on this host over a bounded
+sample of the same workload's tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["sparse_mla_attention_fwd_amd/csrc/smla_kernels.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, per_launch_flops: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"smla_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, budget_s: float):
+    """Time the float64 oracle on the first tokens of the workload until the
+    time budget is used (at least 16 tokens)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads
+    from oracle import sparse_mla_fwd_exact
+
+    w = x["workload"]
+    kv = workloads.to_f64(x["kv"])
+    idx = x["indices"].numpy()
+    done, t_used, chunk = 0, 0.0, 16
+    sparse_mla_fwd_exact(workloads.to_f64(x["q"][:1]), kv, idx[:1], x["sm_scale"], 512)  # warm BLAS
+    while done < w.s_q and (t_used < budget_s or done < 16):
+        sl = slice(done, min(w.s_q, done + chunk))
+        q = workloads.to_f64(x["q"][sl])
+        t0 = time.perf_counter()
+        sparse_mla_fwd_exact(q, kv, idx[sl], x["sm_scale"], 512)
+        t_used += time.perf_counter() - t0
+        done = sl.stop
+    valid = ((idx[:done] >= 0) & (idx[:done] < kv.shape[0])).sum()
+    flops = 2.0 * w.h_q * (576 + 512) * float(valid)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {done} of {w.s_q} tokens of the {w.name} workload, float64 numpy "
+                      f"(gather + two GEMMs + exact softmax per token), {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--b-topk", type=int, default=0)
+    ap.add_argument("--num-splits", type=int, default=-1, help="-1: the workload's own setting")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 skips")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(tokens shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mla_attention_fwd_amd as smla
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    x = workloads.make_inputs(w)
+    q = x["q"].to(dev)
+    idx = x["indices"].to(dev)
+    if w.kv_format == "fp8":
+        kv = smla.pack_fp8_kv(x["kv_codes"], x["kv_scales"], dev)
+        fmt = "fp8"
+    else:
+        kv = x["kv"].to(dev)
+        fmt = "bf16"
+    ns = w.num_splits if args.num_splits < 0 else args.num_splits
+    out = torch.empty((w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.s_q, w.h_q), dtype=torch.float32, device=dev)
+    p = smla.make_params(q, kv, idx, x["sm_scale"], out, lse,
+                         kv_format=smla.SMLA_KV_FP8_E4M3 if fmt == "fp8" else smla.SMLA_KV_BF16,
+                         num_splits=ns, b_topk=args.b_topk)
+    plan_splits, plan_bt = smla.smla_fwd_plan(p)
+    need = smla.smla_fwd_workspace_size(p)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    p.workspace, p.workspace_bytes = ws.data_ptr(), ws.numel()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        smla.smla_fwd(p, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch durations with events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    flops = w.flops
+    value = flops / (ms_per_step / 1e3) / 1e12
+    achieved = flops / avg_launch_s / 1e12
+    traffic = load_traffic(w.name, flops)
+    row_bytes = 1152 if fmt == "bf16" else 640
+    gathered = w.valid_slots * row_bytes
+
+    res = {
+        "metric": "sparse MLA fwd TFLOP/s and % bf16 MFMA peak (h_q=64, topk=2048, d_qk=576)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "s_q": w.s_q, "h_q": w.h_q, "topk": w.topk, "s_kv": w.s_kv,
+                   "d_qk": 576, "d_v": 512, "kv_format": fmt, "num_splits": plan_splits,
+                   "b_topk": plan_bt, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+        "gather": {"bytes_per_launch": gathered, "GB/s": round(gathered / avg_launch_s / 1e9, 1),
+                   "frac_of_hbm_peak": round(gathered / avg_launch_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+    }
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,7 +47,6 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kChunksPerRow = kRowBytesBf16 / 16;   // 72
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // RESCALE_THRES = 6 in natural-log units of the scaled logit; the kernel keeps
@@ -56,15 +55,20 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThresLog2 = 6.0f * kLog2e;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// 16-byte chunk c of tile row r lives at chunk position c ^ swz(r).  With the
-// 1152-byte row pitch this makes (a) 16 lanes reading one chunk column of 16
-// consecutive rows and (b) the transposed 8-byte reads of 4 rows x 32 bytes
-// per 16-lane group hit distinct LDS banks.
-__device__ __forceinline__ int swz(int r) { return (r & 6) | ((r >> 3) & 1); }
-__device__ __forceinline__ int tile_off(int r, int c) {
-  return r * kRowBytesBf16 + ((c ^ swz(r)) << 4);
+// LDS stage layout.  A stage holds BT gathered rows of 72 16-byte chunks.  It
+// is cut into 1 KB units of 8 rows x 8 chunks (one 128-byte line of each of 8
+// rows); unit (m, rb) -- chunk group m = c/8, row block rb = r/8 -- sits at
+// (m·BT/8 + rb)·1 KB.  Inside a unit the 64 chunks are stored chunk-major,
+// slot = (c%8)·8 + r%8, and units of odd rb are rotated by 8 slots (128 bytes).
+//  * Gather: one direct-to-LDS instruction fills one unit, i.e. 8 full lines,
+//    which keeps the random-row gather at full memory efficiency.
+//  * QK operand (16 consecutive rows, one chunk): two 128-byte runs that the
+//    rotation puts on disjoint LDS bank halves.
+//  * V operand (transposed 8-byte reads of 4 rows x 2 chunks per 16 lanes):
+//    each 32-lane half reads one contiguous 256-byte span.
+__device__ __forceinline__ int unit_slot(int c8, int r8, int rb) {
+  return ((c8 ^ (rb & 1)) << 3) | r8;
 }
-
 template <typename T>
 __device__ __forceinline__ T lds_load(const char* base, int off) {
   return *(const LDS_AS T*)((const LDS_AS char*)(const LDS_AS void*)base + off);
@@ -84,6 +88,13 @@ __device__ __forceinline__ void barrier_no_vm_drain() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Keep an MFMA accumulator tile in AGPRs at a non-MFMA definition or use, so
+// that its whole live range stays in the accumulator register file.
+__device__ __forceinline__ f32x4 pin_agpr(f32x4 t) {
+  asm volatile("" : "+a"(t));
+  return t;
 }
 
 __device__ __forceinline__ float wave_max16x4(float v) {
@@ -128,35 +139,65 @@ __device__ int compact_slots(const int32_t* __restrict__ irow, int lo, int hi, i
   return nvalid;
 }
 
-// Enqueue the gather of one block (BT compacted slots) into an LDS stage.
-// Slot positions are contiguous per wave instruction (direct-to-LDS writes go
-// to M0 + 16·lane); each lane fetches the global chunk whose swizzled position
-// is its slot.  Padding slots past the valid count hold the token's first
-// valid row: it is finite, and the softmax gives those slots weight exactly 0.
+// Gather of one block (BT compacted slots) into an LDS stage.  Unit
+// u = m·(BT/8) + rb is filled by one wave instruction; waves take units
+// u = w, w + NW, ... so that each wave keeps a fixed set of row blocks.  Lane
+// l fills slot l of the unit: row 8rb + l%8, chunk 8m + ((l/8) ^ (rb&1)); its
+// global address is one row base plus the immediate 128·m.  Padding slots
+// past the valid count hold the token's first valid row: it is finite and the
+// softmax gives those slots weight exactly 0.
+//
+// The instructions of one block are spread through the MFMA stream of the
+// previous block (a burst of them back-pressures the issuing wave); GatherPlan
+// holds the per-lane row base addresses, GatherPlan::issue(k) sends the k-th
+// instruction of this wave.
 template <int NW, int BT>
-__device__ __forceinline__ void issue_gather_bf16(char* stage, const char* __restrict__ kv,
-                                                  int64_t row_bytes, const int* sidx_blk, int tid) {
-  constexpr int NT = NW * 64;
-  constexpr int CH = BT * kChunksPerRow;
-  constexpr int LPB = (CH + NT - 1) / NT;
-  const int w = tid >> 6;
+struct GatherPlan {
+  static constexpr int R = BT / 8;                    // row blocks
+  static constexpr int UNITS = 9 * R;                 // instructions per block
+  static constexpr int PER_WAVE = (UNITS + NW - 1) / NW;
+  static constexpr int NRB = NW >= R ? 1 : R / NW;    // row blocks per wave
+  const char* base[NRB];
+  char* stage;
+  int w;
+  bool active;
+
+  __device__ __forceinline__ void prepare(char* stg, const char* __restrict__ kv, int64_t row_bytes,
+                                          const int* sidx_blk, int tid, bool on) {
+    const int l = tid & 63;
+    w = tid >> 6;
+    stage = stg;
+    active = on;
+    if (!on) return;
 #pragma unroll
-  for (int k = 0; k < LPB; ++k) {
-    const int slot = k * NT + tid;
-    if (CH % NT == 0 || slot < CH) {
-      const int row = slot / kChunksPerRow;
-      const int pos = slot - row * kChunksPerRow;
-      const int c = pos ^ swz(row);
-      const char* src = kv + (int64_t)sidx_blk[row] * row_bytes + (c << 4);
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (LDS_AS void*)(stage + (k * NT + w * 64) * 16), 16, 0, 0);
+    for (int j = 0; j < NRB; ++j) {
+      const int rb = (w + j * NW) % R;
+      const int c = (l >> 3) ^ (rb & 1);
+      base[j] = kv + (int64_t)sidx_blk[8 * rb + (l & 7)] * row_bytes + (c << 4);
     }
   }
-}
+
+  // k-th instruction of this wave: unit u = k·NW + w.
+  __device__ __forceinline__ void issue(int k) {
+    if (!active) return;
+    const int u = k * NW + w;                          // wave-uniform
+    if (UNITS % NW == 0 || u < UNITS) {
+      const int m = u / R;
+      const int j = NW >= R ? 0 : k % NRB;             // which of this wave's row blocks
+      __builtin_amdgcn_global_load_lds((const void*)(base[j] + 128 * m),
+                                       (LDS_AS void*)(stage + u * 1024), 16, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void issue_all() {
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) issue(k);
+  }
+};
 
 template <int NW, int BT>
 constexpr int loads_per_block() {
-  return (BT * kChunksPerRow + NW * 64 - 1) / (NW * 64);
+  return GatherPlan<NW, BT>::PER_WAVE;
 }
 
 // Wait until at most `pend` later blocks' gathers are outstanding, plus all
@@ -180,48 +221,87 @@ struct State {
   float sumexp;     // this lane's partial running_sumexp (keys 4g..4g+3 of each tile)
 };
 
-// Per-lane LDS byte offsets of the two operand reads.  The chunk swizzle only
-// flips the low three bits of a chunk index, so every step of the unrolled
-// loops adds a compile-time immediate to one of a few per-lane bases.
+// Per-lane LDS byte offsets of the two operand reads (see the stage layout).
+// Every step of the unrolled loops adds a compile-time immediate to one of a
+// few per-lane bases.
+template <int BT>
 struct LaneOffsets {
-  int qk[2];   // K operand, chunk 4s+g of row n: s even / odd
-  int tr[4];   // V operand, row 4g + n/4, chunk 2dt + ((n&3)>>1): dt mod 4
+  int qk[2];   // K operand: row n (+16kt), chunk 4s + g; by s & 1
+  int tr[4];   // V operand: rows 4g + i/4 (+32ks), chunk 2dt + ((i&3)>>1); by dt & 3
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+template <int BT>
+__device__ __forceinline__ LaneOffsets<BT> lane_offsets(int lane) {
   const int g = lane >> 4, n = lane & 15;
-  LaneOffsets o;
+  LaneOffsets<BT> o;
+  // QK: row block 2kt + n/8, row-in-block n%8, chunk-in-group 4(s&1) + g
 #pragma unroll
-  for (int v = 0; v < 2; ++v) o.qk[v] = n * kRowBytesBf16 + (((4 * v + g) ^ swz(n)) << 4);
-  const int row = 4 * g + (n >> 2);
-  const int cadd = (n & 3) >> 1;
+  for (int v = 0; v < 2; ++v)
+    o.qk[v] = ((n >> 3) * 64 + unit_slot(4 * v + g, n & 7, n >> 3)) * 16;
+  // V: row 4g + n/4 -> row block g/2 (+4ks), row-in-block 4(g&1) + n/4;
+  //    chunk 2dt + ((n&3)>>1) -> group dt/4, chunk-in-group 2(dt&3) + ((n&3)>>1)
+  const int rb = g >> 1, r8 = 4 * (g & 1) + (n >> 2);
 #pragma unroll
   for (int v = 0; v < 4; ++v)
-    o.tr[v] = row * kRowBytesBf16 + (((2 * v + cadd) ^ swz(row)) << 4) + (n & 1) * 8;
+    o.tr[v] = (rb * 64 + unit_slot(2 * v + ((n & 3) >> 1), r8, rb)) * 16 + (n & 1) * 8;
   return o;
 }
 
 // One block: QKᵀ, skip-scale online softmax, PV.
-template <int BT>
-__device__ __forceinline__ void compute_block(const char* tile, const LaneOffsets& lo,
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedVmem = 0x010;
+
+// One block: QKᵀ, skip-scale online softmax, PV.  The LDS operands of both
+// products are fetched PF MFMAs ahead through a small rotating register
+// buffer, and the next block's gather instructions are interleaved with the PV
+// MFMAs.
+template <int NW, int BT>
+__device__ __forceinline__ void compute_block(const char* tile, const LaneOffsets<BT>& lo,
                                               const bf16x8 (&qf)[18], State& st,
-                                              int blk, int nvalid, float scale_log2, int lane) {
+                                              int blk, int nvalid, float scale_log2, int lane,
+                                              GatherPlan<NW, BT>& next) {
   constexpr int KT = BT / 16;
+  constexpr int UNIT_GROUP = (BT / 8) * 1024;   // bytes between chunk groups
+  constexpr int NQ = 18 * KT;                   // QK MFMAs
+  constexpr int PF = 8;                         // operand prefetch depth (MFMAs)
   const int g = lane >> 4;
-  // Pᵀ = G·Qᵀ over d_qk = 576 = 18 steps of 32.  Row 16kt + n has the same
-  // swizzle as row n; chunk 4s + g = 8(s/2) + (4(s&1) + g).
-  f32x4 p[KT];
+
+  // ---- Pᵀ = G·Qᵀ over d_qk = 576 = 18 steps of 32.  MFMA i: step s = i / KT,
+  // key tile kt = i % KT.  Even and odd steps accumulate separately so that
+  // 2·KT independent chains are in flight.
+  auto qk_off = [&](int i) {
+    const int s = i / KT, kt = i % KT;
+    return lo.qk[s & 1] + (s >> 1) * UNIT_GROUP + kt * 2048;
+  };
+  f32x4 pe[KT], po[KT];
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) p[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < KT; ++kt) {
+    pe[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    po[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 abuf[PF];
 #pragma unroll
-  for (int s = 0; s < 18; ++s) {
+  for (int i = 0; i < PF; ++i) abuf[i] = lds_load<bf16x8>(tile, qk_off(i));
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const bf16x8 a = lds_load<bf16x8>(tile, lo.qk[s & 1] + kt * 16 * kRowBytesBf16 + (s >> 1) * 128);
-      p[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], p[kt], 0, 0, 0);
+  for (int i = 0; i < NQ; ++i) {
+    const int s = i / KT, kt = i % KT;
+    if (s & 1)
+      po[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], po[kt], 0, 0, 0);
+    else
+      pe[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], pe[kt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + PF < NQ) {
+      abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
   }
-  // Scaled logits in log2 units; slots past the compacted count are masked.
+  f32x4 p[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) p[kt] = pe[kt] + po[kt];
+
+  // ---- scaled logits in log2 units; slots past the compacted count are masked
   float x[KT][4];
   float cur = kNegInf;
   const int j0 = blk * BT + 4 * g;
@@ -243,7 +323,12 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
     // exp2(-inf) = 0 on the first block: the zero state stays zero.
     const float alpha = __builtin_amdgcn_exp2f(st.running_max_for_softmax - rmax);
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) st.o[dt] *= alpha;
+    for (int dt = 0; dt < 32; ++dt) {
+      // The accumulators live in AGPRs (MFMA C/D); pinning the rescaled values
+      // back there keeps the register allocator from moving all 128 of them to
+      // VGPRs around the loop for this rarely taken branch.
+      st.o[dt] = pin_agpr(pin_agpr(st.o[dt]) * alpha);
+    }
     st.sumexp *= alpha;
     st.running_max_for_softmax = rmax;
   }
@@ -257,28 +342,56 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
       st.sumexp += sv[kt][r];
     }
   }
-  // Oᵀ += Vᵀ·Sᵀ, 32 keys per MFMA step.  Lane (g, n) holds S for head n and
-  // keys {32ks + 4g + e, 32ks + 16 + 4g + e}, e < 4; the transposed reads give
-  // the V operand the same key order.
+
+  // ---- Oᵀ += Vᵀ·Sᵀ, 32 keys per MFMA step.  Lane (g, n) holds S for head n
+  // and keys {32ks + 4g + e, 32ks + 16 + 4g + e}, e < 4; the transposed reads
+  // give the V operand the same key order.  MFMA i: ks = i / 32, dt = i % 32.
+  constexpr int NPV = 32 * (BT / 32);
+  constexpr int PFV = 4;
+  constexpr int NDMA = GatherPlan<NW, BT>::PER_WAVE;
+  bf16x8 sb[BT / 32];
 #pragma unroll
   for (int ks = 0; ks < BT / 32; ++ks) {
-    union { uint32_t u[4]; bf16x8 v; } sb;
-    sb.u[0] = pack2_bf16(sv[2 * ks][0], sv[2 * ks][1]);
-    sb.u[1] = pack2_bf16(sv[2 * ks][2], sv[2 * ks][3]);
-    sb.u[2] = pack2_bf16(sv[2 * ks + 1][0], sv[2 * ks + 1][1]);
-    sb.u[3] = pack2_bf16(sv[2 * ks + 1][2], sv[2 * ks + 1][3]);
+    union { uint32_t u[4]; bf16x8 v; } t;
+    t.u[0] = pack2_bf16(sv[2 * ks][0], sv[2 * ks][1]);
+    t.u[1] = pack2_bf16(sv[2 * ks][2], sv[2 * ks][3]);
+    t.u[2] = pack2_bf16(sv[2 * ks + 1][0], sv[2 * ks + 1][1]);
+    t.u[3] = pack2_bf16(sv[2 * ks + 1][2], sv[2 * ks + 1][3]);
+    sb[ks] = t.v;
+  }
+  auto tr_off = [&](int i) {
+    const int ks = i / 32, dt = i % 32;
+    return lo.tr[dt & 3] + (dt >> 2) * UNIT_GROUP + ks * 4096;
+  };
+  auto tr_load = [&](int off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off));
+  };
+  i16x4 va[PFV], vb[PFV];
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      // rows 32ks + 4g + n/4 and 16 rows further; chunk 2dt + .. = 8(dt/4) + ..
-      const int off = lo.tr[dt & 3] + 32 * ks * kRowBytesBf16 + (dt >> 2) * 128;
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off));
-      const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off + 16 * kRowBytesBf16));
-      union { i16x4 h[2]; bf16x8 v; } a;
-      a.h[0] = va;
-      a.h[1] = vb;
-      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, sb.v, st.o[dt], 0, 0, 0);
+  for (int i = 0; i < PFV; ++i) {
+    va[i] = tr_load(tr_off(i));
+    vb[i] = tr_load(tr_off(i) + 2048);
+  }
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    union { i16x4 h[2]; bf16x8 v; } a;
+    a.h[0] = va[i % PFV];
+    a.h[1] = vb[i % PFV];
+    const int dt = i % 32;
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, sb[i / 32], st.o[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (i + PFV < NPV) {
+      va[i % PFV] = tr_load(tr_off(i + PFV));
+      vb[i % PFV] = tr_load(tr_off(i + PFV) + 2048);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    // gather instructions [ceil(i·NDMA/NPV), ceil((i+1)·NDMA/NPV)) go after MFMA i:
+    // all NDMA of them, spread evenly over the NPV MFMAs
+#pragma unroll
+    for (int k = (i * NDMA + NPV - 1) / NPV; k < ((i + 1) * NDMA + NPV - 1) / NPV; ++k) {
+      next.issue(k);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
     }
   }
 }
@@ -324,17 +437,22 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
 
   State st;
 #pragma unroll
-  for (int dt = 0; dt < 32; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 32; ++dt) st.o[dt] = pin_agpr(f32x4{0.f, 0.f, 0.f, 0.f});
   st.running_max = kNegInf;
   st.running_max_for_softmax = kNegInf;
   st.sumexp = 0.f;
 
-  const LaneOffsets lofs = lane_offsets(lane);
+  const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
 
   // Prologue: NST-1 blocks in flight.
 #pragma unroll
-  for (int b = 0; b < NST - 1; ++b)
-    if (b < nblk) issue_gather_bf16<NW, BT>(stages[b], a.kv, a.kv_row_bytes, sidx + b * BT, tid);
+  for (int b = 0; b < NST - 1; ++b) {
+    if (b < nblk) {
+      GatherPlan<NW, BT> gp;
+      gp.prepare(stages[b], a.kv, a.kv_row_bytes, sidx + b * BT, tid, true);
+      gp.issue_all();
+    }
+  }
 
   for (int i0 = 0; i0 < nblk; i0 += NST) {
 #pragma unroll
@@ -343,10 +461,12 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
       if (i < nblk) {
         wait_block<LPB, NST>(min(nblk - 1, i + NST - 2) - i);
         barrier_no_vm_drain();
-        if (i + NST - 1 < nblk)
-          issue_gather_bf16<NW, BT>(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes,
-                                    sidx + (i + NST - 1) * BT, tid);
-        compute_block<BT>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane);
+        // refill the stage freed by block i-1 with block i+NST-1, interleaved
+        // with this block's PV products
+        GatherPlan<NW, BT> gp;
+        gp.prepare(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid,
+                   i + NST - 1 < nblk);
+        compute_block<NW, BT>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
       }
     }
   }
@@ -362,9 +482,10 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
     uint16_t* orow = a.out + (int64_t)token * a.out_st + (int64_t)head * a.out_sh + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
+      const f32x4 o = pin_agpr(st.o[dt]);
       i32x2 v;
-      v[0] = (int)pack2_bf16(st.o[dt][0] * inv, st.o[dt][1] * inv);
-      v[1] = (int)pack2_bf16(st.o[dt][2] * inv, st.o[dt][3] * inv);
+      v[0] = (int)pack2_bf16(o[0] * inv, o[1] * inv);
+      v[1] = (int)pack2_bf16(o[2] * inv, o[3] * inv);
       *(i32x2*)(orow + 16 * dt) = v;
     }
     if (g == 0) a.lse[(int64_t)token * a.lse_st + head] = lse;
@@ -372,7 +493,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
     const int64_t part = ((int64_t)token * a.num_splits + split) * a.h_q + head;
     float* orow = a.ws_o + part * kDv + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(f32x4*)(orow + 16 * dt) = st.o[dt] * inv;
+    for (int dt = 0; dt < 32; ++dt) *(f32x4*)(orow + 16 * dt) = pin_agpr(st.o[dt]) * inv;
     if (g == 0) a.ws_lse[part] = lse;
   }
 }
