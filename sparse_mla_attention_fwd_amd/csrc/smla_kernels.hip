@@ -160,15 +160,12 @@ struct GatherPlan {
   const char* base[NRB];
   char* stage;
   int w;
-  bool active;
 
   __device__ __forceinline__ void prepare(char* stg, const char* __restrict__ kv, int64_t row_bytes,
-                                          const int* sidx_blk, int tid, bool on) {
+                                          const int* sidx_blk, int tid) {
     const int l = tid & 63;
     w = tid >> 6;
     stage = stg;
-    active = on;
-    if (!on) return;
 #pragma unroll
     for (int j = 0; j < NRB; ++j) {
       const int rb = (w + j * NW) % R;
@@ -179,7 +176,6 @@ struct GatherPlan {
 
   // k-th instruction of this wave: unit u = k·NW + w.
   __device__ __forceinline__ void issue(int k) {
-    if (!active) return;
     const int u = k * NW + w;                          // wave-uniform
     if (UNITS % NW == 0 || u < UNITS) {
       const int m = u / R;
@@ -249,15 +245,11 @@ __device__ __forceinline__ LaneOffsets<BT> lane_offsets(int lane) {
 
 // One block: QKᵀ, skip-scale online softmax, PV.
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-constexpr int kSchedVmem = 0x010;
-
 // One block: QKᵀ, skip-scale online softmax, PV.  The LDS operands of both
 // products are fetched PF MFMAs ahead through a small rotating register
-// buffer, and the next block's gather instructions are interleaved with the PV
-// MFMAs.
-template <int NW, int BT>
+// buffer (scheduling fences keep the order), and, with REFILL, the next
+// block's gather instructions are interleaved with the PV MFMAs.
+template <int NW, int BT, bool REFILL>
 __device__ __forceinline__ void compute_block(const char* tile, const LaneOffsets<BT>& lo,
                                               const bf16x8 (&qf)[18], State& st,
                                               int blk, int nvalid, float scale_log2, int lane,
@@ -265,7 +257,9 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   constexpr int KT = BT / 16;
   constexpr int UNIT_GROUP = (BT / 8) * 1024;   // bytes between chunk groups
   constexpr int NQ = 18 * KT;                   // QK MFMAs
-  constexpr int PF = 8;                         // operand prefetch depth (MFMAs)
+  // operand prefetch depth in MFMAs; 512-thread workgroups have 256 registers
+  // per lane and cannot afford a deep buffer
+  constexpr int PF = NW >= 8 ? 2 : 8;
   const int g = lane >> 4;
 
   // ---- Pᵀ = G·Qᵀ over d_qk = 576 = 18 steps of 32.  MFMA i: step s = i / KT,
@@ -284,6 +278,7 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   bf16x8 abuf[PF];
 #pragma unroll
   for (int i = 0; i < PF; ++i) abuf[i] = lds_load<bf16x8>(tile, qk_off(i));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     const int s = i / KT, kt = i % KT;
@@ -291,11 +286,8 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
       po[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], po[kt], 0, 0, 0);
     else
       pe[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], pe[kt], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (i + PF < NQ) {
-      abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
+    if (i + PF < NQ) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
+    __builtin_amdgcn_sched_barrier(0);
   }
   f32x4 p[KT];
 #pragma unroll
@@ -347,7 +339,7 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   // and keys {32ks + 4g + e, 32ks + 16 + 4g + e}, e < 4; the transposed reads
   // give the V operand the same key order.  MFMA i: ks = i / 32, dt = i % 32.
   constexpr int NPV = 32 * (BT / 32);
-  constexpr int PFV = 4;
+  constexpr int PFV = NW >= 8 ? 2 : 4;
   constexpr int NDMA = GatherPlan<NW, BT>::PER_WAVE;
   bf16x8 sb[BT / 32];
 #pragma unroll
@@ -373,6 +365,7 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
     va[i] = tr_load(tr_off(i));
     vb[i] = tr_load(tr_off(i) + 2048);
   }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     union { i16x4 h[2]; bf16x8 v; } a;
@@ -380,19 +373,17 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
     a.h[1] = vb[i % PFV];
     const int dt = i % 32;
     st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, sb[i / 32], st.o[dt], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if (i + PFV < NPV) {
       va[i % PFV] = tr_load(tr_off(i + PFV));
       vb[i % PFV] = tr_load(tr_off(i + PFV) + 2048);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
     // gather instructions [ceil(i·NDMA/NPV), ceil((i+1)·NDMA/NPV)) go after MFMA i:
     // all NDMA of them, spread evenly over the NPV MFMAs
+    if constexpr (REFILL) {
 #pragma unroll
-    for (int k = (i * NDMA + NPV - 1) / NPV; k < ((i + 1) * NDMA + NPV - 1) / NPV; ++k) {
-      next.issue(k);
-      __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+      for (int k = (i * NDMA + NPV - 1) / NPV; k < ((i + 1) * NDMA + NPV - 1) / NPV; ++k) next.issue(k);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -449,24 +440,52 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   for (int b = 0; b < NST - 1; ++b) {
     if (b < nblk) {
       GatherPlan<NW, BT> gp;
-      gp.prepare(stages[b], a.kv, a.kv_row_bytes, sidx + b * BT, tid, true);
+      gp.prepare(stages[b], a.kv, a.kv_row_bytes, sidx + b * BT, tid);
       gp.issue_all();
     }
   }
 
-  for (int i0 = 0; i0 < nblk; i0 += NST) {
+  // Steady state: every block i refills the stage freed by block i-1 with
+  // block i+NST-1 (the refill is interleaved with block i's PV products).
+  // Groups of NST blocks keep every stage index a compile-time constant.
+  int i0 = 0;
+  for (; i0 + 2 * NST - 2 < nblk; i0 += NST) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      const int i = i0 + s;
+      wait_block<LPB, NST>(NST - 2);
+      barrier_no_vm_drain();
+      GatherPlan<NW, BT> gp;
+      gp.prepare(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid);
+      compute_block<NW, BT, true>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
+    }
+  }
+  // Tail: the last blocks, refilling while blocks remain.
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+    const int i = i0 + s;
+    if (i < nblk) {
+      wait_block<LPB, NST>(min(nblk - 1, i + NST - 2) - i);
+      barrier_no_vm_drain();
+      GatherPlan<NW, BT> gp;
+      if (i + NST - 1 < nblk) {
+        gp.prepare(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid);
+        compute_block<NW, BT, true>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
+      } else {
+        compute_block<NW, BT, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
+      }
+    }
+  }
+  // The tail loop runs at most NST blocks: i0 + 2·NST - 2 >= nblk there.
+  for (i0 += NST; i0 < nblk; i0 += NST) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
       const int i = i0 + s;
       if (i < nblk) {
         wait_block<LPB, NST>(min(nblk - 1, i + NST - 2) - i);
         barrier_no_vm_drain();
-        // refill the stage freed by block i-1 with block i+NST-1, interleaved
-        // with this block's PV products
         GatherPlan<NW, BT> gp;
-        gp.prepare(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid,
-                   i + NST - 1 < nblk);
-        compute_block<NW, BT>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
+        compute_block<NW, BT, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
       }
     }
   }
