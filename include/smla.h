@@ -65,8 +65,9 @@ extern "C" {
 #define SMLA_FP8_ROW_BYTES 640
 
 /* Largest number of slots one workgroup handles; the planner splits the topk
- * range of a token into parts no larger than this. */
+ * range of a token into parts no larger than this (bf16 KV / fp8 KV). */
 #define SMLA_MAX_SLOTS_PER_SPLIT 2048
+#define SMLA_MAX_SLOTS_PER_SPLIT_FP8 1536
 
 typedef enum smla_status {
   SMLA_OK = 0,
@@ -115,7 +116,8 @@ typedef struct smla_fwd_params {
   /* tuning: 0 lets the planner choose.
    *   num_splits: parts of each token's topk range, each run by its own
    *               workgroup and merged by log-sum-exp (decode occupancy).
-   *   b_topk:     slots per block of the online softmax: 32 or 64. */
+   *   b_topk:     slots per block of the online softmax: 32 or 64 (bf16 KV),
+ *               32 (fp8 KV). */
   int32_t num_splits;
   int32_t b_topk;
 

@@ -27,6 +27,7 @@ FP8_GROUP = 128
 FP8_NUM_GROUPS = 5
 FP8_ROW_BYTES = 640
 MAX_SLOTS_PER_SPLIT = 2048
+MAX_SLOTS_PER_SPLIT_FP8 = 1536
 
 # Every symbol include/smla.h declares.
 EXPORTS = ("smla_fwd_plan", "smla_fwd_workspace_size", "smla_fwd", "smla_pack_fp8_kv_host",

@@ -12,6 +12,8 @@ constexpr int kDv = 512;
 constexpr int kRowBytesBf16 = kDqk * 2;   // 1152: nine 128-byte lines
 constexpr int kFp8RowBytes = 640;         // 576 codes + 5 float32 scales + pad
 constexpr int kMaxSlotsPerSplit = 2048;
+// fp8 KV: the raw-row ring and two bf16 stages leave room for 1536 indices
+constexpr int kMaxSlotsPerSplitFp8 = 1536;
 
 // Everything one launch of the forward kernel needs, by value.
 struct FwdArgs {

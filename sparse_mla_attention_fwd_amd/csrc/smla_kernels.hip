@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "smla_internal.h"
 
 namespace smla {
@@ -247,13 +249,22 @@ __device__ __forceinline__ LaneOffsets<BT> lane_offsets(int lane) {
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 // One block: QKᵀ, skip-scale online softmax, PV.  The LDS operands of both
 // products are fetched PF MFMAs ahead through a small rotating register
-// buffer (scheduling fences keep the order), and, with REFILL, the next
-// block's gather instructions are interleaved with the PV MFMAs.
-template <int NW, int BT, bool REFILL>
+// buffer (scheduling fences keep the order).  With REFILL the gather
+// instructions of a later block are interleaved with the PV MFMAs; with SIDE
+// the side work (the fp8 dequantisation of the next block) is interleaved with
+// the QK MFMAs.
+// No side work in the QK loop (bf16 KV).
+struct NoSideWork {
+  static constexpr int PER_THREAD = 0;
+  __device__ __forceinline__ void run(int) {}
+};
+
+template <int NW, int BT, bool REFILL, bool SIDE, bool FP8, class Gather, class Side>
 __device__ __forceinline__ void compute_block(const char* tile, const LaneOffsets<BT>& lo,
                                               const bf16x8 (&qf)[18], State& st,
                                               int blk, int nvalid, float scale_log2, int lane,
-                                              GatherPlan<NW, BT>& next) {
+                                              Gather& next, Side& side,
+                                              const float* stile = nullptr) {
   constexpr int KT = BT / 16;
   constexpr int UNIT_GROUP = (BT / 8) * 1024;   // bytes between chunk groups
   constexpr int NQ = 18 * KT;                   // QK MFMAs
@@ -263,18 +274,21 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   const int g = lane >> 4;
 
   // ---- Pᵀ = G·Qᵀ over d_qk = 576 = 18 steps of 32.  MFMA i: step s = i / KT,
-  // key tile kt = i % KT.  Even and odd steps accumulate separately so that
-  // 2·KT independent chains are in flight.
+  // key tile kt = i % KT.  bf16 KV: even and odd steps accumulate separately so
+  // that 2·KT independent chains are in flight.  fp8 KV: the tile holds the
+  // E4M3 codes (exact in bf16) and each 128-column scale group accumulates on
+  // its own; the per-row group scales are applied below in fp32.
   auto qk_off = [&](int i) {
     const int s = i / KT, kt = i % KT;
     return lo.qk[s & 1] + (s >> 1) * UNIT_GROUP + kt * 2048;
   };
-  f32x4 pe[KT], po[KT];
+  constexpr int NACC = FP8 ? 5 : 2;
+  auto acc_of = [](int s) { return FP8 ? s / 4 : (s & 1); };
+  f32x4 pacc[NACC][KT];
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    pe[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    po[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int c = 0; c < NACC; ++c)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) pacc[c][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 abuf[PF];
 #pragma unroll
   for (int i = 0; i < PF; ++i) abuf[i] = lds_load<bf16x8>(tile, qk_off(i));
@@ -282,16 +296,42 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     const int s = i / KT, kt = i % KT;
-    if (s & 1)
-      po[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], po[kt], 0, 0, 0);
-    else
-      pe[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], pe[kt], 0, 0, 0);
+    pacc[acc_of(s)][kt] =
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], pacc[acc_of(s)][kt], 0, 0, 0);
     if (i + PF < NQ) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
+    if constexpr (SIDE) {
+      constexpr int NS = Side::PER_THREAD;
+#pragma unroll
+      for (int k = (i * NS + NQ - 1) / NQ; k < ((i + 1) * NS + NQ - 1) / NQ; ++k) side.run(k);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   f32x4 p[KT];
+  // fp8: group scales of this lane's keys 16kt + 4g + r, from the block's
+  // group-major scale tile [5][BT]
+  float ksc[KT][4][5];
+  if constexpr (FP8) {
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) p[kt] = pe[kt] + po[kt];
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int c = 0; c < 5; ++c) {
+        const f32x4 a4 = lds_load<f32x4>((const char*)stile, (c * BT + 16 * kt + 4 * g) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ksc[kt][r][c] = a4[r];
+      }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = 0.f;
+#pragma unroll
+        for (int c = 0; c < 5; ++c) v = fmaf(ksc[kt][r][c], pacc[c][kt][r], v);
+        p[kt][r] = v;
+      }
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) p[kt] = pacc[0][kt] + pacc[1][kt];
+  }
 
   // ---- scaled logits in log2 units; slots past the compacted count are masked
   float x[KT][4];
@@ -340,16 +380,28 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   // give the V operand the same key order.  MFMA i: ks = i / 32, dt = i % 32.
   constexpr int NPV = 32 * (BT / 32);
   constexpr int PFV = NW >= 8 ? 2 : 4;
-  constexpr int NDMA = GatherPlan<NW, BT>::PER_WAVE;
-  bf16x8 sb[BT / 32];
+  constexpr int NDMA = Gather::PER_WAVE;
+  // S as the bf16 B operand; fp8 KV: one operand per 128-column V group with
+  // that row's group scale folded in, so that the V operand stays the exact code.
+  constexpr int NSB = FP8 ? 4 : 1;
+  bf16x8 sb[NSB][BT / 32];
 #pragma unroll
-  for (int ks = 0; ks < BT / 32; ++ks) {
-    union { uint32_t u[4]; bf16x8 v; } t;
-    t.u[0] = pack2_bf16(sv[2 * ks][0], sv[2 * ks][1]);
-    t.u[1] = pack2_bf16(sv[2 * ks][2], sv[2 * ks][3]);
-    t.u[2] = pack2_bf16(sv[2 * ks + 1][0], sv[2 * ks + 1][1]);
-    t.u[3] = pack2_bf16(sv[2 * ks + 1][2], sv[2 * ks + 1][3]);
-    sb[ks] = t.v;
+  for (int gv = 0; gv < NSB; ++gv) {
+#pragma unroll
+    for (int ks = 0; ks < BT / 32; ++ks) {
+      float w[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          w[h][r] = FP8 ? sv[2 * ks + h][r] * ksc[2 * ks + h][r][gv] : sv[2 * ks + h][r];
+      union { uint32_t u[4]; bf16x8 v; } t;
+      t.u[0] = pack2_bf16(w[0][0], w[0][1]);
+      t.u[1] = pack2_bf16(w[0][2], w[0][3]);
+      t.u[2] = pack2_bf16(w[1][0], w[1][1]);
+      t.u[3] = pack2_bf16(w[1][2], w[1][3]);
+      sb[gv][ks] = t.v;
+    }
   }
   auto tr_off = [&](int i) {
     const int ks = i / 32, dt = i % 32;
@@ -372,7 +424,7 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
     a.h[0] = va[i % PFV];
     a.h[1] = vb[i % PFV];
     const int dt = i % 32;
-    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, sb[i / 32], st.o[dt], 0, 0, 0);
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, sb[FP8 ? dt / 8 : 0][i / 32], st.o[dt], 0, 0, 0);
     if (i + PFV < NPV) {
       va[i % PFV] = tr_load(tr_off(i + PFV));
       vb[i % PFV] = tr_load(tr_off(i + PFV) + 2048);
@@ -384,6 +436,53 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
       for (int k = (i * NDMA + NPV - 1) / NPV; k < ((i + 1) * NDMA + NPV - 1) / NPV; ++k) next.issue(k);
     }
     __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Load Q for this wave's 16 heads: B operand of Pᵀ = G·Qᵀ, lane (g, n) holds
+// Q[head n][32s + 8g .. 32s + 8g + 7].
+__device__ __forceinline__ void load_q(const FwdArgs& a, int token, int head, int g, bf16x8 (&qf)[18]) {
+  const uint16_t* qrow = a.q + (int64_t)token * a.q_st + (int64_t)head * a.q_sh + 8 * g;
+#pragma unroll
+  for (int s = 0; s < 18; ++s) qf[s] = *(const bf16x8*)(qrow + 32 * s);
+}
+
+__device__ __forceinline__ void init_state(State& st) {
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) st.o[dt] = pin_agpr(f32x4{0.f, 0.f, 0.f, 0.f});
+  st.running_max = kNegInf;
+  st.running_max_for_softmax = kNegInf;
+  st.sumexp = 0.f;
+}
+
+// Epilogue: total running_sumexp per head, normalise, write the output (or
+// the split partial: normalised output and lse of this part).
+template <bool SPLIT>
+__device__ __forceinline__ void write_output(const FwdArgs& a, State& st, int token, int split,
+                                             int head, int g, int nvalid) {
+  float l = st.sumexp;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const bool empty = nvalid == 0;
+  const float inv = empty ? 0.f : 1.0f / l;
+  const float lse = empty ? kNegInf : (st.running_max_for_softmax + __builtin_amdgcn_logf(l)) * kLn2;
+  if constexpr (!SPLIT) {
+    uint16_t* orow = a.out + (int64_t)token * a.out_st + (int64_t)head * a.out_sh + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      const f32x4 o = pin_agpr(st.o[dt]);
+      i32x2 v;
+      v[0] = (int)pack2_bf16(o[0] * inv, o[1] * inv);
+      v[1] = (int)pack2_bf16(o[2] * inv, o[3] * inv);
+      *(i32x2*)(orow + 16 * dt) = v;
+    }
+    if (g == 0) a.lse[(int64_t)token * a.lse_st + head] = lse;
+  } else {
+    const int64_t part = ((int64_t)token * a.num_splits + split) * a.h_q + head;
+    float* orow = a.ws_o + part * kDv + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) *(f32x4*)(orow + 16 * dt) = pin_agpr(st.o[dt]) * inv;
+    if (g == 0) a.ws_lse[part] = lse;
   }
 }
 
@@ -416,24 +515,14 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   for (int j = nvalid + tid; j < nblk * BT; j += NW * 64) sidx[j] = sidx[0];
   __syncthreads();
 
-  // Q for this wave's 16 heads: B operand of Pᵀ = G·Qᵀ, lane (g, n) holds
-  // Q[head n][32s + 8g .. 32s + 8g + 7].
   const int head = w * 16 + n;
   bf16x8 qf[18];
-  {
-    const uint16_t* qrow = a.q + (int64_t)token * a.q_st + (int64_t)head * a.q_sh + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 18; ++s) qf[s] = *(const bf16x8*)(qrow + 32 * s);
-  }
-
+  load_q(a, token, head, g, qf);
   State st;
-#pragma unroll
-  for (int dt = 0; dt < 32; ++dt) st.o[dt] = pin_agpr(f32x4{0.f, 0.f, 0.f, 0.f});
-  st.running_max = kNegInf;
-  st.running_max_for_softmax = kNegInf;
-  st.sumexp = 0.f;
+  init_state(st);
 
   const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
+  NoSideWork nside;
 
   // Prologue: NST-1 blocks in flight.
 #pragma unroll
@@ -457,7 +546,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
       barrier_no_vm_drain();
       GatherPlan<NW, BT> gp;
       gp.prepare(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid);
-      compute_block<NW, BT, true>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
+      compute_block<NW, BT, true, false, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp, nside);
     }
   }
   // Tail: the last blocks, refilling while blocks remain.
@@ -470,9 +559,9 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
       GatherPlan<NW, BT> gp;
       if (i + NST - 1 < nblk) {
         gp.prepare(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid);
-        compute_block<NW, BT, true>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
+        compute_block<NW, BT, true, false, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp, nside);
       } else {
-        compute_block<NW, BT, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
+        compute_block<NW, BT, false, false, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp, nside);
       }
     }
   }
@@ -485,36 +574,211 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
         wait_block<LPB, NST>(min(nblk - 1, i + NST - 2) - i);
         barrier_no_vm_drain();
         GatherPlan<NW, BT> gp;
-        compute_block<NW, BT, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp);
+        compute_block<NW, BT, false, false, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp, nside);
       }
     }
   }
 
-  // Epilogue: total running_sumexp per head, normalise, write.
-  float l = st.sumexp;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  const bool empty = nvalid == 0;
-  const float inv = empty ? 0.f : 1.0f / l;
-  const float lse = empty ? kNegInf : (st.running_max_for_softmax + __builtin_amdgcn_logf(l)) * kLn2;
-  if constexpr (!SPLIT) {
-    uint16_t* orow = a.out + (int64_t)token * a.out_st + (int64_t)head * a.out_sh + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const f32x4 o = pin_agpr(st.o[dt]);
-      i32x2 v;
-      v[0] = (int)pack2_bf16(o[0] * inv, o[1] * inv);
-      v[1] = (int)pack2_bf16(o[2] * inv, o[3] * inv);
-      *(i32x2*)(orow + 16 * dt) = v;
-    }
-    if (g == 0) a.lse[(int64_t)token * a.lse_st + head] = lse;
-  } else {
-    const int64_t part = ((int64_t)token * a.num_splits + split) * a.h_q + head;
-    float* orow = a.ws_o + part * kDv + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(f32x4*)(orow + 16 * dt) = pin_agpr(st.o[dt]) * inv;
-    if (g == 0) a.ws_lse[part] = lse;
+  write_output<SPLIT>(a, st, token, split, head, g, nvalid);
+}
+
+// ---------------------------------------------------------------------------
+// fp8 KV cache.  A packed row is 576 E4M3 codes followed by five float32
+// scales (one per 128 columns) and padding to 640 bytes: a token's data and
+// scales sit side by side, as the page's section "Decoding KV Cache Layout 优化"
+// recommends, so one gather brings both.  Raw rows land in an LDS ring by
+// direct-to-LDS loads; the workgroup converts the codes of block i+1 to bf16
+// (exactly) in the stage layout above while computing block i, so the MFMA
+// code is shared, and folds the scales in fp32 (dequantisation without any
+// rounding of K or V).
+constexpr int kFp8RowChunks = kFp8RowBytes / 16;   // 40
+
+// Gather of one block of packed rows into a raw LDS slot, row-major; wave
+// instruction k fills 64 consecutive 16-byte chunks (whole lines of ~2 rows).
+template <int NW>
+struct RawGatherFp8 {
+  static constexpr int BT = 32;
+  static constexpr int UNITS = BT * kFp8RowChunks / 64;   // 20 instructions per block
+  static constexpr int PER_WAVE = (UNITS + NW - 1) / NW;
+  const char* kv;
+  int64_t row_bytes;
+  const int* sidx_blk;
+  char* slot;
+  int tid;
+
+  __device__ __forceinline__ void prepare(char* raw, const char* __restrict__ kvp, int64_t rb,
+                                          const int* sb, int t) {
+    slot = raw;
+    kv = kvp;
+    row_bytes = rb;
+    sidx_blk = sb;
+    tid = t;
   }
+  __device__ __forceinline__ void issue(int k) {
+    const int w = tid >> 6, l = tid & 63;
+    const int u = k * NW + w;                              // wave-uniform
+    if (UNITS % NW == 0 || u < UNITS) {
+      const int c = u * 64 + l;
+      const int row = c / kFp8RowChunks, ch = c - row * kFp8RowChunks;
+      const char* src = kv + (int64_t)sidx_blk[row] * row_bytes + (ch << 4);
+      __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(slot + u * 1024), 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void issue_all() {
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) issue(k);
+  }
+};
+
+// Conversion of one raw block into a bf16 stage: task c converts 16 codes of
+// row c/36 (columns 16·(c%36) .. +15).  Every E4M3 value is exactly a bf16
+// value, so the stage holds the codes without rounding; the row's group
+// scales are applied in fp32 by the block computation (to the QK partial sums
+// of each group, and to S for each V group).  The scales are copied to a
+// separate small tile: once converted, the raw slot may be refilled by any
+// wave while others still compute on the block.
+template <int NW>
+struct DequantFp8 {
+  static constexpr int BT = 32;
+  static constexpr int TASKS = BT * (kDqk / 16);            // 1152
+  static constexpr int NT = NW * 64;
+  static constexpr int PER_THREAD = (TASKS + NT - 1) / NT;
+  const char* raw;
+  char* tile;
+  float* stile;   // [5][BT] group-major copy of the block's scales
+  int tid;
+
+  __device__ __forceinline__ void run(int k) {
+    // Threads past the last task redo it: the same bytes written twice.
+    const int c = min(k * NT + tid, TASKS - 1);
+    const int r = c / 36, cc = c - r * 36;
+    const i32x4 codes = lds_load<i32x4>(raw, r * kFp8RowBytes + cc * 16);
+    // every task also copies one scale of its row (groups repeat: same value)
+    const int gs = cc % 5;
+    *(LDS_AS float*)((LDS_AS char*)(LDS_AS void*)stile + (gs * BT + r) * 4) =
+        lds_load<float>(raw, r * kFp8RowBytes + kDqk + gs * 4);
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // two codes -> two exact fp32 values -> two exact bf16 values
+      const auto f = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(codes[j >> 1], true)
+                             : __builtin_amdgcn_cvt_pk_f32_fp8(codes[j >> 1], false);
+      o[j] = pack2_bf16(f[0], f[1]);
+    }
+    // bf16 chunks 2cc and 2cc+1 of row r in the unit layout
+    const int rb = r >> 3, r8 = r & 7;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = 2 * cc + h;
+      const int off = ((ch >> 3) * (BT / 8) + rb) * 1024 + unit_slot(ch & 7, r8, rb) * 16;
+      *(LDS_AS i32x4*)((LDS_AS char*)(LDS_AS void*)tile + off) =
+          i32x4{(int)o[4 * h], (int)o[4 * h + 1], (int)o[4 * h + 2], (int)o[4 * h + 3]};
+    }
+  }
+  __device__ __forceinline__ void run_all() {
+#pragma unroll
+    for (int k = 0; k < PER_THREAD; ++k) run(k);
+  }
+};
+
+template <int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
+  constexpr int BT = 32;
+  constexpr int NSTR = 4;                                  // raw ring depth
+  constexpr int LPB = RawGatherFp8<NW>::PER_WAVE;
+  constexpr int RAW = BT * kFp8RowBytes;
+  constexpr int TILE = BT * kRowBytesBf16;
+  __shared__ __attribute__((aligned(1024))) char rw0[RAW];
+  __shared__ __attribute__((aligned(1024))) char rw1[RAW];
+  __shared__ __attribute__((aligned(1024))) char rw2[RAW];
+  __shared__ __attribute__((aligned(1024))) char rw3[RAW];
+  __shared__ __attribute__((aligned(1024))) char tl0[TILE];
+  __shared__ __attribute__((aligned(1024))) char tl1[TILE];
+  __shared__ __attribute__((aligned(16))) float sc0[5 * BT];
+  __shared__ __attribute__((aligned(16))) float sc1[5 * BT];
+  __shared__ int sidx[kMaxSlotsPerSplitFp8 + BT];
+  __shared__ int swcnt[NW];
+  char* const raws[4] = {rw0, rw1, rw2, rw3};
+  char* const tiles[2] = {tl0, tl1};
+  float* const stiles[2] = {sc0, sc1};
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int token = blockIdx.x / a.num_splits;
+  const int split = blockIdx.x - token * a.num_splits;
+  const int lo = split * a.slots_per_split;
+  const int hi = min(a.topk, lo + a.slots_per_split);
+
+  const int nvalid = compact_slots<NW>(a.idx + (int64_t)token * a.idx_st, lo, hi, a.s_kv, sidx,
+                                       swcnt, tid);
+  const int nblk = (nvalid + BT - 1) / BT;
+  for (int j = nvalid + tid; j < nblk * BT; j += NW * 64) sidx[j] = sidx[0];
+  __syncthreads();
+
+  const int head = w * 16 + n;
+  bf16x8 qf[18];
+  load_q(a, token, head, g, qf);
+  State st;
+  init_state(st);
+  const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
+
+  // Prologue: raw blocks 0..NSTR-1 in flight, block 0 dequantised.
+#pragma unroll
+  for (int b = 0; b < NSTR; ++b) {
+    if (b < nblk) {
+      RawGatherFp8<NW> rg;
+      rg.prepare(raws[b], a.kv, a.kv_row_bytes, sidx + b * BT, tid);
+      rg.issue_all();
+    }
+  }
+  if (nblk > 0) {
+    wait_block<LPB, NSTR>(min(nblk - 1, NSTR - 1));
+    barrier_no_vm_drain();
+    DequantFp8<NW> dq{raws[0], tiles[0], stiles[0], tid};
+    dq.run_all();
+  }
+
+  // Block i: wait for raw block i+1, then (after the barrier) refill the raw
+  // slot of block i with block i+NSTR during the PV products and dequantise
+  // block i+1 into the other bf16 tile during the QK products.
+  auto step = [&](auto S, int i, auto REFILL, auto DEQ) {
+    constexpr int s = decltype(S)::value;
+    if constexpr (decltype(DEQ)::value)
+      wait_block<LPB, NSTR>(min(nblk - 1, i + NSTR - 1) - (i + 1));
+    else
+      wait_block<LPB, NSTR>(0);
+    barrier_no_vm_drain();
+    RawGatherFp8<NW> rg;
+    if constexpr (decltype(REFILL)::value)
+      rg.prepare(raws[s], a.kv, a.kv_row_bytes, sidx + (i + NSTR) * BT, tid);
+    DequantFp8<NW> dq{raws[(s + 1) % NSTR], tiles[(s + 1) & 1], stiles[(s + 1) & 1], tid};
+    compute_block<NW, BT, decltype(REFILL)::value, decltype(DEQ)::value, true>(
+        tiles[s & 1], lofs, qf, st, i, nvalid, a.scale_log2, lane, rg, dq, stiles[s & 1]);
+  };
+  using T = std::integral_constant<bool, true>;
+  using F = std::integral_constant<bool, false>;
+  int i0 = 0;
+  for (; i0 + 2 * NSTR - 1 < nblk; i0 += NSTR) {
+    step(std::integral_constant<int, 0>{}, i0 + 0, T{}, T{});
+    step(std::integral_constant<int, 1>{}, i0 + 1, T{}, T{});
+    step(std::integral_constant<int, 2>{}, i0 + 2, T{}, T{});
+    step(std::integral_constant<int, 3>{}, i0 + 3, T{}, T{});
+  }
+  for (; i0 < nblk; i0 += NSTR) {
+    auto tail = [&](auto S) {
+      const int i = i0 + decltype(S)::value;
+      if (i >= nblk) return;
+      if (i + NSTR < nblk) step(S, i, T{}, T{});
+      else if (i + 1 < nblk) step(S, i, F{}, T{});
+      else step(S, i, F{}, F{});
+    };
+    tail(std::integral_constant<int, 0>{});
+    tail(std::integral_constant<int, 1>{});
+    tail(std::integral_constant<int, 2>{});
+    tail(std::integral_constant<int, 3>{});
+  }
+
+  write_output<SPLIT>(a, st, token, split, head, g, nvalid);
 }
 
 // Log-sum-exp merge of split partials: one thread per (token, head, 8 columns).
@@ -572,15 +836,34 @@ hipError_t launch_nw(const FwdArgs& a, int b_topk, hipStream_t stream) {
 
 }  // namespace
 
+template <int NW>
+hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)((int64_t)a.s_q * a.num_splits);
+  if (a.num_splits > 1)
+    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream) {
-  if (fp8) return hipErrorNotSupported;
   hipError_t e;
-  switch (a.h_q) {
-    case 16: e = launch_nw<1>(a, b_topk, stream); break;
-    case 32: e = launch_nw<2>(a, b_topk, stream); break;
-    case 64: e = launch_nw<4>(a, b_topk, stream); break;
-    case 128: e = launch_nw<8>(a, b_topk, stream); break;
-    default: return hipErrorInvalidValue;
+  if (fp8) {
+    switch (a.h_q) {
+      case 16: e = launch_fp8<1>(a, stream); break;
+      case 32: e = launch_fp8<2>(a, stream); break;
+      case 64: e = launch_fp8<4>(a, stream); break;
+      case 128: e = launch_fp8<8>(a, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.h_q) {
+      case 16: e = launch_nw<1>(a, b_topk, stream); break;
+      case 32: e = launch_nw<2>(a, b_topk, stream); break;
+      case 64: e = launch_nw<4>(a, b_topk, stream); break;
+      case 128: e = launch_nw<8>(a, b_topk, stream); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   if (e != hipSuccess || a.num_splits <= 1) return e;
   const int64_t threads = (int64_t)a.s_q * a.h_q * (kDv / 8);

@@ -118,7 +118,7 @@ def test_empty_batch_is_a_no_op():
 def test_workspace_required_for_split_plans():
     lib = _lib.load()
     p = _params(num_splits=3)
-    assert _lib.smla_fwd_plan(p) == (3, 64)
+    assert _lib.smla_fwd_plan(p) == (3, 32)
     need = _lib.smla_fwd_workspace_size(p)
     parts = 4 * 3 * 16
     assert need == parts * 512 * 4 + ((parts * 4 + 255) // 256) * 256
@@ -127,18 +127,21 @@ def test_workspace_required_for_split_plans():
     assert lib.smla_fwd(ctypes.byref(p), None) == _lib.SMLA_ERR_WORKSPACE
 
 
-@pytest.mark.parametrize("name,splits", [("tiny", None), ("prefill", 1), ("causal", 1), ("decode", 4)])
+@pytest.mark.parametrize("name,splits", [("tiny", None), ("prefill", 1), ("causal", 1), ("decode", 4),
+                                         ("decode_fp8", None)])
 def test_plans_of_named_workloads(name, splits):
     import workloads
     w = workloads.WORKLOADS[name]
+    fp8 = w.kv_format == "fp8"
     p = _params(s_q=w.s_q, h_q=w.h_q, topk=w.topk, s_kv=w.s_kv, num_splits=w.num_splits,
                 q_stride_token=w.h_q * 576, out_stride_token=w.h_q * 512, lse_stride_token=w.h_q,
-                indices_stride_token=w.topk)
+                indices_stride_token=w.topk, kv_format=int(fp8), kv_stride_row=640 if fp8 else 576)
     ns, bt = _lib.smla_fwd_plan(p)
     if splits is not None:
         assert ns == splits
     assert bt in (32, 64)
-    assert (w.topk + ns - 1) // ns <= _lib.MAX_SLOTS_PER_SPLIT
+    cap = _lib.MAX_SLOTS_PER_SPLIT_FP8 if fp8 else _lib.MAX_SLOTS_PER_SPLIT
+    assert (w.topk + ns - 1) // ns <= cap
 
 
 def test_topk_beyond_one_split_needs_more_parts():
@@ -148,6 +151,20 @@ def test_topk_beyond_one_split_needs_more_parts():
     p.num_splits = 0
     ns, _ = _lib.smla_fwd_plan(p)
     assert ns >= 3
+
+
+def test_fp8_plan_limits():
+    p = _params(kv_format=1, kv_stride_row=640, topk=2048, indices_stride_token=2048, num_splits=1)
+    with pytest.raises(_lib.SmlaError):
+        _lib.smla_fwd_plan(p)          # 2048 slots exceed one fp8 part
+    p.num_splits = 2
+    assert _lib.smla_fwd_plan(p) == (2, 32)
+    p.b_topk = 64
+    with pytest.raises(_lib.SmlaError):
+        _lib.smla_fwd_plan(p)
+    p.b_topk, p.kv_stride_row = 0, 600
+    with pytest.raises(_lib.SmlaError):
+        _lib.smla_fwd_plan(p)
 
 
 def test_pack_fp8_rows_host():

@@ -226,6 +226,40 @@ def test_causal_full_size_sampled(dev):
     _sampled(dev, x, tokens)
 
 
+@pytest.mark.parametrize("h_q", [16, 64])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_fp8_random_cases(dev, h_q, num_splits):
+    x = workloads.make_random(s_q=3, h_q=h_q, topk=300, s_kv=2000, seed=60 + h_q + num_splits,
+                              kv_format="fp8", invalid_frac=0.2, q_mult=2.0)
+    x["indices"][2, :] = -1
+    out, lse = run_gpu(dev, x, num_splits=num_splits)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"fp8 h{h_q} splits={num_splits}")
+
+
+def test_fp8_single_row_matches_dequant(dev):
+    """All slots on one row: out is that row's V = code * scale.  The codes are
+    used exactly and the scale enters through the bf16 S operand, so each
+    element is within two bf16 roundings (unit roundoff 2^-8 each, so 2^-7
+    relative) of the exact value;
+    lse is the row's logit plus ln(topk)."""
+    x = workloads.make_random(s_q=2, h_q=64, topk=64, s_kv=100, seed=8, kv_format="fp8")
+    x["indices"][0, :] = 17
+    x["indices"][1, :] = 99
+    out, lse = run_gpu(dev, x, num_splits=1)
+    for t, r in enumerate((17, 99)):
+        row = dequant_fp8_rows(x["kv_codes"][r:r + 1].numpy(), x["kv_scales"][r:r + 1].numpy())[0]
+        v = row[:512]
+        assert np.all(np.abs(out[t] - v) <= 2.0 ** -7 * np.abs(v) + 1e-30)
+        xr = (workloads.to_f64(x["q"][t]) @ row) * x["sm_scale"]
+        assert np.abs(lse[t] - (xr + math.log(64))).max() < 1e-4
+
+
+def test_decode_fp8_full_size_sampled(dev):
+    x = workloads.make_inputs("decode_fp8")
+    _sampled(dev, x, np.array([0, 1, 63, 64, 126, 127]))
+
+
 def test_decode_full_size_all_tokens(dev):
     x = workloads.make_inputs("decode")
     _sampled(dev, x, np.arange(64), num_splits=4)
