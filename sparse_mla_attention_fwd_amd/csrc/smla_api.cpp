@@ -121,7 +121,7 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   pl.slots_per_split = (p->topk + ns - 1) / ns;
   // the parts actually used may be fewer than ns after rounding up
   pl.num_splits = (p->topk + pl.slots_per_split - 1) / pl.slots_per_split;
-  if ((int64_t)p->s_q * pl.num_splits > 2147483647LL)
+  if ((int64_t)p->s_q * pl.num_splits * (p->h_q > 64 ? 2 : 1) + 8 > 2147483647LL)
     return fail(SMLA_ERR_UNSUPPORTED, "grid of s_q*num_splits workgroups is too large");
   pl.workspace_bytes = 0;
   if (pl.num_splits > 1) {
@@ -190,6 +190,7 @@ smla_status smla_fwd(const smla_fwd_params* p, void* stream) {
   a.topk = p->topk;
   a.slots_per_split = pl.slots_per_split;
   a.num_splits = pl.num_splits;
+  a.head_groups = p->h_q > 64 ? p->h_q / 64 : 1;
   a.s_kv = p->s_kv;
   a.scale_log2 = p->sm_scale * 1.4426950408889634f;
   const hipError_t e = smla::launch_fwd(a, pl.b_topk, p->kv_format == SMLA_KV_FP8_E4M3,

@@ -30,6 +30,7 @@ struct FwdArgs {
   float* ws_o;              // [s_q, num_splits, h_q, 512] fp32 (split plans)
   float* ws_lse;            // [s_q, num_splits, h_q] fp32 (split plans)
   int32_t s_q, h_q, topk, slots_per_split, num_splits;
+  int32_t head_groups;      // workgroups per (token, split): h_q / 64, at least 1
   int64_t s_kv;
   float scale_log2;         // sm_scale * log2(e)
 };

@@ -92,6 +92,17 @@ __device__ __forceinline__ void barrier_no_vm_drain() {
   asm volatile("" ::: "memory");
 }
 
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).  Every
+// register array below is indexed with constants only, which keeps it out of
+// scratch memory regardless of the unroller's size limits.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Keep an MFMA accumulator tile in AGPRs at a non-MFMA definition or use, so
 // that its whole live range stays in the accumulator register file.
 __device__ __forceinline__ f32x4 pin_agpr(f32x4 t) {
@@ -278,12 +289,12 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   // that 2·KT independent chains are in flight.  fp8 KV: the tile holds the
   // E4M3 codes (exact in bf16) and each 128-column scale group accumulates on
   // its own; the per-row group scales are applied below in fp32.
-  auto qk_off = [&](int i) {
+  auto qk_off = [&](int i) __attribute__((always_inline)) {
     const int s = i / KT, kt = i % KT;
     return lo.qk[s & 1] + (s >> 1) * UNIT_GROUP + kt * 2048;
   };
   constexpr int NACC = FP8 ? 5 : 2;
-  auto acc_of = [](int s) { return FP8 ? s / 4 : (s & 1); };
+  auto acc_of = [](int s) constexpr { return FP8 ? s / 4 : (s & 1); };
   f32x4 pacc[NACC][KT];
 #pragma unroll
   for (int c = 0; c < NACC; ++c)
@@ -293,19 +304,20 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
 #pragma unroll
   for (int i = 0; i < PF; ++i) abuf[i] = lds_load<bf16x8>(tile, qk_off(i));
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int s = i / KT, kt = i % KT;
+  static_for<0, NQ>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    constexpr int s = i / KT, kt = i % KT;
     pacc[acc_of(s)][kt] =
         __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], pacc[acc_of(s)][kt], 0, 0, 0);
-    if (i + PF < NQ) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
+    if constexpr (i + PF < NQ) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
     if constexpr (SIDE) {
+      // side tasks [ceil(i·NS/NQ), ceil((i+1)·NS/NQ)) go after MFMA i
       constexpr int NS = Side::PER_THREAD;
-#pragma unroll
-      for (int k = (i * NS + NQ - 1) / NQ; k < ((i + 1) * NS + NQ - 1) / NQ; ++k) side.run(k);
+      static_for<(i * NS + NQ - 1) / NQ, ((i + 1) * NS + NQ - 1) / NQ>(
+          [&](auto K) __attribute__((always_inline)) { side.run(decltype(K)::value); });
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
+  });
   f32x4 p[KT];
   // fp8: group scales of this lane's keys 16kt + 4g + r, from the block's
   // group-major scale tile [5][BT]
@@ -403,11 +415,11 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
       sb[gv][ks] = t.v;
     }
   }
-  auto tr_off = [&](int i) {
+  auto tr_off = [&](int i) __attribute__((always_inline)) {
     const int ks = i / 32, dt = i % 32;
     return lo.tr[dt & 3] + (dt >> 2) * UNIT_GROUP + ks * 4096;
   };
-  auto tr_load = [&](int off) {
+  auto tr_load = [&](int off) __attribute__((always_inline)) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off));
   };
@@ -418,25 +430,48 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
     vb[i] = tr_load(tr_off(i) + 2048);
   }
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NPV; ++i) {
+  static_for<0, NPV>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
     union { i16x4 h[2]; bf16x8 v; } a;
     a.h[0] = va[i % PFV];
     a.h[1] = vb[i % PFV];
-    const int dt = i % 32;
+    constexpr int dt = i % 32;
     st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, sb[FP8 ? dt / 8 : 0][i / 32], st.o[dt], 0, 0, 0);
-    if (i + PFV < NPV) {
+    if constexpr (i + PFV < NPV) {
       va[i % PFV] = tr_load(tr_off(i + PFV));
       vb[i % PFV] = tr_load(tr_off(i + PFV) + 2048);
     }
     // gather instructions [ceil(i·NDMA/NPV), ceil((i+1)·NDMA/NPV)) go after MFMA i:
     // all NDMA of them, spread evenly over the NPV MFMAs
     if constexpr (REFILL) {
-#pragma unroll
-      for (int k = (i * NDMA + NPV - 1) / NPV; k < ((i + 1) * NDMA + NPV - 1) / NPV; ++k) next.issue(k);
+      static_for<(i * NDMA + NPV - 1) / NPV, ((i + 1) * NDMA + NPV - 1) / NPV>(
+          [&](auto K) __attribute__((always_inline)) { next.issue(decltype(K)::value); });
     }
     __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// Work item of this workgroup: (token, split of its slots, group of 64 heads).
+// With several head groups (h_q = 128) the groups of one item get workgroup
+// ids 8 apart: ids are dealt round-robin to the 8 XCDs, so both land on the
+// same XCD at nearly the same time and the second gather of the item's rows
+// mostly hits that XCD's L2.  Returns false for padding workgroups.
+struct WorkItem {
+  int token, split, head0;
+};
+__device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& wi) {
+  const int items = a.s_q * a.num_splits;
+  int item = blockIdx.x, hg = 0;
+  if (a.head_groups > 1) {
+    const int rest = blockIdx.x >> 3;
+    hg = rest % a.head_groups;
+    item = (rest / a.head_groups) * 8 + (blockIdx.x & 7);
   }
+  if (item >= items) return false;
+  wi.token = item / a.num_splits;
+  wi.split = item - wi.token * a.num_splits;
+  wi.head0 = hg * 64;
+  return true;
 }
 
 // Load Q for this wave's 16 heads: B operand of Pᵀ = G·Qᵀ, lane (g, n) holds
@@ -501,10 +536,11 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   __shared__ int swcnt[NW];
   char* const stages[4] = {st0, st1, st2, st3};
 
+  WorkItem wi;
+  if (!work_item(a, wi)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
-  const int token = blockIdx.x / a.num_splits;
-  const int split = blockIdx.x - token * a.num_splits;
+  const int token = wi.token, split = wi.split;
   const int lo = split * a.slots_per_split;
   const int hi = min(a.topk, lo + a.slots_per_split);
 
@@ -515,7 +551,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   for (int j = nvalid + tid; j < nblk * BT; j += NW * 64) sidx[j] = sidx[0];
   __syncthreads();
 
-  const int head = w * 16 + n;
+  const int head = wi.head0 + w * 16 + n;
   bf16x8 qf[18];
   load_q(a, token, head, g, qf);
   State st;
@@ -702,10 +738,11 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   char* const tiles[2] = {tl0, tl1};
   float* const stiles[2] = {sc0, sc1};
 
+  WorkItem wi;
+  if (!work_item(a, wi)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
-  const int token = blockIdx.x / a.num_splits;
-  const int split = blockIdx.x - token * a.num_splits;
+  const int token = wi.token, split = wi.split;
   const int lo = split * a.slots_per_split;
   const int hi = min(a.topk, lo + a.slots_per_split);
 
@@ -715,7 +752,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   for (int j = nvalid + tid; j < nblk * BT; j += NW * 64) sidx[j] = sidx[0];
   __syncthreads();
 
-  const int head = w * 16 + n;
+  const int head = wi.head0 + w * 16 + n;
   bf16x8 qf[18];
   load_q(a, token, head, g, qf);
   State st;
@@ -741,7 +778,8 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   // Block i: wait for raw block i+1, then (after the barrier) refill the raw
   // slot of block i with block i+NSTR during the PV products and dequantise
   // block i+1 into the other bf16 tile during the QK products.
-  auto step = [&](auto S, int i, auto REFILL, auto DEQ) {
+  // (always inlined: the state captured by reference must stay in registers)
+  auto step = [&](auto S, int i, auto REFILL, auto DEQ) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;
     if constexpr (decltype(DEQ)::value)
       wait_block<LPB, NSTR>(min(nblk - 1, i + NSTR - 1) - (i + 1));
@@ -765,7 +803,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
     step(std::integral_constant<int, 3>{}, i0 + 3, T{}, T{});
   }
   for (; i0 < nblk; i0 += NSTR) {
-    auto tail = [&](auto S) {
+    auto tail = [&](auto S) __attribute__((always_inline)) {
       const int i = i0 + decltype(S)::value;
       if (i >= nblk) return;
       if (i + NSTR < nblk) step(S, i, T{}, T{});
@@ -818,10 +856,16 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
   if (q8 == 0) a.lse[token * a.lse_st + head] = z > 0.f ? m + __logf(z) : kNegInf;
 }
 
+unsigned grid_size(const FwdArgs& a) {
+  const int64_t items = (int64_t)a.s_q * a.num_splits;
+  if (a.head_groups == 1) return (unsigned)items;
+  return (unsigned)(((items + 7) / 8) * 8 * a.head_groups);
+}
+
 template <int NW, int BT, bool SPLIT>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
   constexpr int NST = BT == 32 ? 4 : 2;
-  const unsigned grid = (unsigned)((int64_t)a.s_q * a.num_splits);
+  const unsigned grid = grid_size(a);
   hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT>), dim3(grid), dim3(NW * 64), 0,
                      stream, a);
   return hipGetLastError();
@@ -838,7 +882,7 @@ hipError_t launch_nw(const FwdArgs& a, int b_topk, hipStream_t stream) {
 
 template <int NW>
 hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)((int64_t)a.s_q * a.num_splits);
+  const unsigned grid = grid_size(a);
   if (a.num_splits > 1)
     hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
   else
@@ -852,16 +896,16 @@ hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream
     switch (a.h_q) {
       case 16: e = launch_fp8<1>(a, stream); break;
       case 32: e = launch_fp8<2>(a, stream); break;
-      case 64: e = launch_fp8<4>(a, stream); break;
-      case 128: e = launch_fp8<8>(a, stream); break;
+      case 64:
+      case 128: e = launch_fp8<4>(a, stream); break;   // 128: two head groups
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (a.h_q) {
       case 16: e = launch_nw<1>(a, b_topk, stream); break;
       case 32: e = launch_nw<2>(a, b_topk, stream); break;
-      case 64: e = launch_nw<4>(a, b_topk, stream); break;
-      case 128: e = launch_nw<8>(a, b_topk, stream); break;
+      case 64:
+      case 128: e = launch_nw<4>(a, b_topk, stream); break;   // 128: two head groups
       default: return hipErrorInvalidValue;
     }
   }
