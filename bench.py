@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--b-topk", type=int, default=0)
     ap.add_argument("--num-splits", type=int, default=-1, help="-1: the workload's own setting")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 skips")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -109,6 +111,17 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # A plain copy of known size: under rocprofv3 its FETCH_SIZE / WRITE_SIZE
+        # give the factor that turns those counters into bytes.
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
     w = workloads.WORKLOADS[args.workload]
     x = workloads.make_inputs(w)
     q = x["q"].to(dev)
