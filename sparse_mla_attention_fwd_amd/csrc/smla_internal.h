@@ -33,6 +33,11 @@ struct FwdArgs {
   int32_t head_groups;      // workgroups per (token, split): h_q / 64, at least 1
   int64_t s_kv;
   float scale_log2;         // sm_scale * log2(e)
+  // Bytes of KV reachable with 32-bit offsets from kv: (s_kv - 1) * kv_row_bytes
+  // + the row length when that fits in 32 bits (the gathers then use buffer
+  // loads, whose hardware range check also covers every access), else 0 (the
+  // gathers use 64-bit global addresses).
+  uint32_t kv_window_bytes;
 };
 
 // Launch the forward pass (and the split combine when num_splits > 1).

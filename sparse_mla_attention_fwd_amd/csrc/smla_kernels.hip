@@ -152,38 +152,74 @@ __device__ int compact_slots(const int32_t* __restrict__ irow, int lo, int hi, i
   return nvalid;
 }
 
+// Source of the gathers.  With BUF the whole KV lies in a 32-bit window:
+// buffer loads (MUBUF) from one uniform resource, each lane adding its 32-bit
+// row offset (the hardware also range-checks every access against the
+// window).  Otherwise 64-bit global addresses (FLAT-encoded global loads).
+// The buffer form is preferred: the compiler's wait-count tracking treats a
+// FLAT direct-to-LDS load as a possible LDS access and then drains every
+// pending LDS read (lgkmcnt(0)) after it, which breaks the operand prefetch
+// of the products.
+template <bool BUF>
+struct KvSource {
+  const char* kv;
+  __amdgpu_buffer_rsrc_t rsrc;
+  KvSource() = default;
+  __device__ __forceinline__ KvSource(const char* p, uint32_t window) : kv(p) {
+    if constexpr (BUF)
+      // word 3 = 0x00020000: 32-bit data format, no swizzle, no index stride
+      rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)window, 0x00020000);
+  }
+  // One 16-byte direct-to-LDS load of byte row_off + add (add: wave-uniform)
+  // into lds + 16·lane.
+  __device__ __forceinline__ void load16(LDS_AS void* lds, uint32_t voff, const char* vaddr,
+                                         int add) const {
+    if constexpr (BUF)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, voff, add, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((const void*)(vaddr + add), lds, 16, 0, 0);
+  }
+};
+
 // Gather of one block (BT compacted slots) into an LDS stage.  Unit
 // u = m·(BT/8) + rb is filled by one wave instruction; waves take units
 // u = w, w + NW, ... so that each wave keeps a fixed set of row blocks.  Lane
 // l fills slot l of the unit: row 8rb + l%8, chunk 8m + ((l/8) ^ (rb&1)); its
-// global address is one row base plus the immediate 128·m.  Padding slots
-// past the valid count hold the token's first valid row: it is finite and the
-// softmax gives those slots weight exactly 0.
+// address is one row base plus 128·m.  Padding slots past the valid count
+// hold the token's first valid row: it is finite and the softmax gives those
+// slots weight exactly 0.
 //
 // The instructions of one block are spread through the MFMA stream of the
 // previous block (a burst of them back-pressures the issuing wave); GatherPlan
-// holds the per-lane row base addresses, GatherPlan::issue(k) sends the k-th
+// holds the per-lane row bases, GatherPlan::issue(k) sends the k-th
 // instruction of this wave.
-template <int NW, int BT>
+template <int NW, int BT, bool BUF>
 struct GatherPlan {
   static constexpr int R = BT / 8;                    // row blocks
   static constexpr int UNITS = 9 * R;                 // instructions per block
   static constexpr int PER_WAVE = (UNITS + NW - 1) / NW;
   static constexpr int NRB = NW >= R ? 1 : R / NW;    // row blocks per wave
-  const char* base[NRB];
+  uint32_t voff[NRB];                                 // BUF: byte offsets in the window
+  const char* base[NRB];                              // !BUF: addresses
+  KvSource<BUF> src;
   char* stage;
   int w;
 
-  __device__ __forceinline__ void prepare(char* stg, const char* __restrict__ kv, int64_t row_bytes,
+  __device__ __forceinline__ void prepare(char* stg, const KvSource<BUF>& src, int64_t row_bytes,
                                           const int* sidx_blk, int tid) {
     const int l = tid & 63;
-    w = tid >> 6;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
     stage = stg;
+    this->src = src;
 #pragma unroll
     for (int j = 0; j < NRB; ++j) {
       const int rb = (w + j * NW) % R;
       const int c = (l >> 3) ^ (rb & 1);
-      base[j] = kv + (int64_t)sidx_blk[8 * rb + (l & 7)] * row_bytes + (c << 4);
+      const int row = sidx_blk[8 * rb + (l & 7)];
+      if constexpr (BUF)
+        voff[j] = (uint32_t)row * (uint32_t)row_bytes + (uint32_t)(c << 4);
+      else
+        base[j] = src.kv + (int64_t)row * row_bytes + (c << 4);
     }
   }
 
@@ -193,11 +229,9 @@ struct GatherPlan {
     if (UNITS % NW == 0 || u < UNITS) {
       const int m = u / R;
       const int j = NW >= R ? 0 : k % NRB;             // which of this wave's row blocks
-      __builtin_amdgcn_global_load_lds((const void*)(base[j] + 128 * m),
-                                       (LDS_AS void*)(stage + u * 1024), 16, 0, 0);
+      src.load16((LDS_AS void*)(stage + u * 1024), voff[j], base[j], 128 * m);
     }
   }
-
   __device__ __forceinline__ void issue_all() {
 #pragma unroll
     for (int k = 0; k < PER_WAVE; ++k) issue(k);
@@ -206,7 +240,7 @@ struct GatherPlan {
 
 template <int NW, int BT>
 constexpr int loads_per_block() {
-  return GatherPlan<NW, BT>::PER_WAVE;
+  return GatherPlan<NW, BT, true>::PER_WAVE;
 }
 
 // Wait until at most `pend` later blocks' gathers are outstanding, plus all
@@ -521,7 +555,7 @@ __device__ __forceinline__ void write_output(const FwdArgs& a, State& st, int to
   }
 }
 
-template <int NW, int BT, int NST, bool SPLIT>
+template <int NW, int BT, int NST, bool SPLIT, bool BUF>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   constexpr int LPB = loads_per_block<NW, BT>();
   constexpr int TILE = BT * kRowBytesBf16;
@@ -559,13 +593,14 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
 
   const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
   NoSideWork nside;
+  const KvSource<BUF> src(a.kv, a.kv_window_bytes);
 
   // Prologue: NST-1 blocks in flight.
 #pragma unroll
   for (int b = 0; b < NST - 1; ++b) {
     if (b < nblk) {
-      GatherPlan<NW, BT> gp;
-      gp.prepare(stages[b], a.kv, a.kv_row_bytes, sidx + b * BT, tid);
+      GatherPlan<NW, BT, BUF> gp;
+      gp.prepare(stages[b], src, a.kv_row_bytes, sidx + b * BT, tid);
       gp.issue_all();
     }
   }
@@ -580,8 +615,8 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
       const int i = i0 + s;
       wait_block<LPB, NST>(NST - 2);
       barrier_no_vm_drain();
-      GatherPlan<NW, BT> gp;
-      gp.prepare(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid);
+      GatherPlan<NW, BT, BUF> gp;
+      gp.prepare(stages[(s + NST - 1) % NST], src, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid);
       compute_block<NW, BT, true, false, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp, nside);
     }
   }
@@ -592,9 +627,9 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
     if (i < nblk) {
       wait_block<LPB, NST>(min(nblk - 1, i + NST - 2) - i);
       barrier_no_vm_drain();
-      GatherPlan<NW, BT> gp;
+      GatherPlan<NW, BT, BUF> gp;
       if (i + NST - 1 < nblk) {
-        gp.prepare(stages[(s + NST - 1) % NST], a.kv, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid);
+        gp.prepare(stages[(s + NST - 1) % NST], src, a.kv_row_bytes, sidx + (i + NST - 1) * BT, tid);
         compute_block<NW, BT, true, false, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp, nside);
       } else {
         compute_block<NW, BT, false, false, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp, nside);
@@ -609,7 +644,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
       if (i < nblk) {
         wait_block<LPB, NST>(min(nblk - 1, i + NST - 2) - i);
         barrier_no_vm_drain();
-        GatherPlan<NW, BT> gp;
+        GatherPlan<NW, BT, BUF> gp;
         compute_block<NW, BT, false, false, false>(stages[s], lofs, qf, st, i, nvalid, a.scale_log2, lane, gp, nside);
       }
     }
@@ -631,33 +666,37 @@ constexpr int kFp8RowChunks = kFp8RowBytes / 16;   // 40
 
 // Gather of one block of packed rows into a raw LDS slot, row-major; wave
 // instruction k fills 64 consecutive 16-byte chunks (whole lines of ~2 rows).
-template <int NW>
+template <int NW, bool BUF>
 struct RawGatherFp8 {
   static constexpr int BT = 32;
   static constexpr int UNITS = BT * kFp8RowChunks / 64;   // 20 instructions per block
   static constexpr int PER_WAVE = (UNITS + NW - 1) / NW;
-  const char* kv;
+  KvSource<BUF> src;
   int64_t row_bytes;
   const int* sidx_blk;
   char* slot;
   int tid;
 
-  __device__ __forceinline__ void prepare(char* raw, const char* __restrict__ kvp, int64_t rb,
+  __device__ __forceinline__ void prepare(char* raw, const KvSource<BUF>& s, int64_t rb,
                                           const int* sb, int t) {
     slot = raw;
-    kv = kvp;
+    src = s;
     row_bytes = rb;
     sidx_blk = sb;
     tid = t;
   }
   __device__ __forceinline__ void issue(int k) {
-    const int w = tid >> 6, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int u = k * NW + w;                              // wave-uniform
     if (UNITS % NW == 0 || u < UNITS) {
       const int c = u * 64 + l;
       const int row = c / kFp8RowChunks, ch = c - row * kFp8RowChunks;
-      const char* src = kv + (int64_t)sidx_blk[row] * row_bytes + (ch << 4);
-      __builtin_amdgcn_global_load_lds((const void*)src, (LDS_AS void*)(slot + u * 1024), 16, 0, 0);
+      const int kvrow = sidx_blk[row];
+      if constexpr (BUF)
+        src.load16((LDS_AS void*)(slot + u * 1024), (uint32_t)kvrow * (uint32_t)row_bytes + (ch << 4),
+                   nullptr, 0);
+      else
+        src.load16((LDS_AS void*)(slot + u * 1024), 0, src.kv + (int64_t)kvrow * row_bytes + (ch << 4), 0);
     }
   }
   __device__ __forceinline__ void issue_all() {
@@ -717,11 +756,11 @@ struct DequantFp8 {
   }
 };
 
-template <int NW, bool SPLIT>
+template <int NW, bool SPLIT, bool BUF>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   constexpr int BT = 32;
   constexpr int NSTR = 4;                                  // raw ring depth
-  constexpr int LPB = RawGatherFp8<NW>::PER_WAVE;
+  constexpr int LPB = RawGatherFp8<NW, BUF>::PER_WAVE;
   constexpr int RAW = BT * kFp8RowBytes;
   constexpr int TILE = BT * kRowBytesBf16;
   __shared__ __attribute__((aligned(1024))) char rw0[RAW];
@@ -758,13 +797,14 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   State st;
   init_state(st);
   const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
+  const KvSource<BUF> src(a.kv, a.kv_window_bytes);
 
   // Prologue: raw blocks 0..NSTR-1 in flight, block 0 dequantised.
 #pragma unroll
   for (int b = 0; b < NSTR; ++b) {
     if (b < nblk) {
-      RawGatherFp8<NW> rg;
-      rg.prepare(raws[b], a.kv, a.kv_row_bytes, sidx + b * BT, tid);
+      RawGatherFp8<NW, BUF> rg;
+      rg.prepare(raws[b], src, a.kv_row_bytes, sidx + b * BT, tid);
       rg.issue_all();
     }
   }
@@ -786,9 +826,9 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
     else
       wait_block<LPB, NSTR>(0);
     barrier_no_vm_drain();
-    RawGatherFp8<NW> rg;
+    RawGatherFp8<NW, BUF> rg;
     if constexpr (decltype(REFILL)::value)
-      rg.prepare(raws[s], a.kv, a.kv_row_bytes, sidx + (i + NSTR) * BT, tid);
+      rg.prepare(raws[s], src, a.kv_row_bytes, sidx + (i + NSTR) * BT, tid);
     DequantFp8<NW> dq{raws[(s + 1) % NSTR], tiles[(s + 1) & 1], stiles[(s + 1) & 1], tid};
     compute_block<NW, BT, decltype(REFILL)::value, decltype(DEQ)::value, true>(
         tiles[s & 1], lofs, qf, st, i, nvalid, a.scale_log2, lane, rg, dq, stiles[s & 1]);
@@ -866,8 +906,12 @@ template <int NW, int BT, bool SPLIT>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
   constexpr int NST = BT == 32 ? 4 : 2;
   const unsigned grid = grid_size(a);
-  hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT>), dim3(grid), dim3(NW * 64), 0,
-                     stream, a);
+  if (a.kv_window_bytes)
+    hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, true>), dim3(grid), dim3(NW * 64), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, false>), dim3(grid), dim3(NW * 64), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
@@ -880,14 +924,19 @@ hipError_t launch_nw(const FwdArgs& a, int b_topk, hipStream_t stream) {
 
 }  // namespace
 
-template <int NW>
-hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
+template <int NW, bool BUF>
+hipError_t launch_fp8_src(const FwdArgs& a, hipStream_t stream) {
   const unsigned grid = grid_size(a);
   if (a.num_splits > 1)
-    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, true, BUF>), dim3(grid), dim3(NW * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, false, BUF>), dim3(grid), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
+  return a.kv_window_bytes ? launch_fp8_src<NW, true>(a, stream) : launch_fp8_src<NW, false>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream) {
