@@ -32,14 +32,17 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["sparse_mla_attention_fwd_amd/csrc/smla_kernels.hip"]
+CSRC = os.path.join(ROOT, "sparse_mla_attention_fwd_amd", "csrc")
 
 
 def kernel_hash() -> str:
+    """sha256[:16] over the device sources (csrc/*.hip, *.cuh, *.h in name
+    order): a traffic summary applies only to the kernels it was taken on."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".cuh", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import os
 import shutil
+from concurrent.futures import ThreadPoolExecutor
 import subprocess
 import sys
 
@@ -14,7 +15,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsmla.so")
-SOURCES = ["smla_kernels.hip", "smla_api.cpp"]
+# The forward kernels are split over several translation units (one per group
+# of launch configurations) so that they compile in parallel.
+SOURCES = ["smla_fwd_fp8_w4.hip", "smla_fwd_fp8_w1w2.hip", "smla_fwd_bf16_w4_b32.hip",
+           "smla_fwd_bf16_w4_b64.hip", "smla_fwd_bf16_w1.hip", "smla_fwd_bf16_w2.hip",
+           "smla_launch.hip", "smla_api.cpp"]
 ARCH = "gfx950"
 
 
@@ -37,11 +42,9 @@ def build(verbose: bool = False) -> str:
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         "-Wall", "-Wno-unused-function",
     ]
-    objs = []
-    for src in SOURCES:
+    def compile_one(src: str) -> str:
         obj = os.path.join(objdir, src + ".o")
-        lang = ["-x", "hip"]
-        cmd = [cc, *common, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *common, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,7 +53,11 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{err}")
         if verbose and err.strip():
             print(err, file=sys.stderr)
-        objs.append(obj)
+        return obj
+
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the gfx950 sparse MLA forward kernels and the
+// split combine: vector types, constants, wait/barrier primitives, the LDS
+// stage layout, compile-time loops and small cross-lane helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "smla_internal.h"
+
+namespace smla {
+namespace {
+
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// RESCALE_THRES = 6 in natural-log units of the scaled logit; the kernel keeps
+// logits in log2 units (exp2 is the native instruction), so the same test reads
+// running_max - running_max_for_softmax > 6·log2(e).
+constexpr float kRescaleThresLog2 = 6.0f * kLog2e;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// LDS stage layout.  A stage holds BT gathered rows of 72 16-byte chunks.  It
+// is cut into 1 KB units of 8 rows x 8 chunks (one 128-byte line of each of 8
+// rows); unit (m, rb) -- chunk group m = c/8, row block rb = r/8 -- sits at
+// (m·BT/8 + rb)·1 KB.  Inside a unit the 64 chunks are stored chunk-major,
+// slot = (c%8)·8 + r%8, and units of odd rb are rotated by 8 slots (128 bytes).
+//  * Gather: one direct-to-LDS instruction fills one unit, i.e. 8 full lines,
+//    which keeps the random-row gather at full memory efficiency.
+//  * QK operand (16 consecutive rows, one chunk): two 128-byte runs that the
+//    rotation puts on disjoint LDS bank halves.
+//  * V operand (transposed 8-byte reads of 4 rows x 2 chunks per 16 lanes):
+//    each 32-lane half reads one contiguous 256-byte span.
+__device__ __forceinline__ int unit_slot(int c8, int r8, int rb) {
+  return ((c8 ^ (rb & 1)) << 3) | r8;
+}
+template <typename T>
+__device__ __forceinline__ T lds_load(const char* base, int off) {
+  return *(const LDS_AS T*)((const LDS_AS char*)(const LDS_AS void*)base + off);
+}
+
+// s_waitcnt with vmcnt = vm (clamped to the 6-bit field) and lgkmcnt = 0.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  constexpr int v = VM > 63 ? 63 : VM;
+  __builtin_amdgcn_s_waitcnt((v & 0xF) | ((v >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Workgroup barrier that orders LDS traffic but does not drain outstanding
+// direct-to-LDS gathers (a __syncthreads fence would wait for every one).
+// Callers wait for their own loads first.
+__device__ __forceinline__ void barrier_no_vm_drain() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).  Every
+// register array below is indexed with constants only, which keeps it out of
+// scratch memory regardless of the unroller's size limits.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Keep an MFMA accumulator tile in AGPRs at a non-MFMA definition or use, so
+// that its whole live range stays in the accumulator register file.
+__device__ __forceinline__ f32x4 pin_agpr(f32x4 t) {
+  asm volatile("" : "+a"(t));
+  return t;
+}
+
+__device__ __forceinline__ float wave_max16x4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+}  // namespace
+}  // namespace smla

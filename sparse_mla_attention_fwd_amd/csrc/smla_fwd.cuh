@@ -31,95 +31,15 @@
 //     a rescale is a per-lane scalar multiply.
 //   * Decode: split-topk partials (normalised output + lse) merged by a
 //     log-sum-exp combine kernel.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+//
+// This header holds the kernels as templates; the smla_fwd_*.hip units each
+// instantiate a subset of the launch configurations (compiled in parallel).
+#pragma once
 
-#include <type_traits>
-
-#include "smla_internal.h"
+#include "smla_common.cuh"
 
 namespace smla {
 namespace {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(4))) int i32x4;
-typedef __attribute__((ext_vector_type(2))) int i32x2;
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-// RESCALE_THRES = 6 in natural-log units of the scaled logit; the kernel keeps
-// logits in log2 units (exp2 is the native instruction), so the same test reads
-// running_max - running_max_for_softmax > 6·log2(e).
-constexpr float kRescaleThresLog2 = 6.0f * kLog2e;
-constexpr float kNegInf = -__builtin_huge_valf();
-
-// LDS stage layout.  A stage holds BT gathered rows of 72 16-byte chunks.  It
-// is cut into 1 KB units of 8 rows x 8 chunks (one 128-byte line of each of 8
-// rows); unit (m, rb) -- chunk group m = c/8, row block rb = r/8 -- sits at
-// (m·BT/8 + rb)·1 KB.  Inside a unit the 64 chunks are stored chunk-major,
-// slot = (c%8)·8 + r%8, and units of odd rb are rotated by 8 slots (128 bytes).
-//  * Gather: one direct-to-LDS instruction fills one unit, i.e. 8 full lines,
-//    which keeps the random-row gather at full memory efficiency.
-//  * QK operand (16 consecutive rows, one chunk): two 128-byte runs that the
-//    rotation puts on disjoint LDS bank halves.
-//  * V operand (transposed 8-byte reads of 4 rows x 2 chunks per 16 lanes):
-//    each 32-lane half reads one contiguous 256-byte span.
-__device__ __forceinline__ int unit_slot(int c8, int r8, int rb) {
-  return ((c8 ^ (rb & 1)) << 3) | r8;
-}
-template <typename T>
-__device__ __forceinline__ T lds_load(const char* base, int off) {
-  return *(const LDS_AS T*)((const LDS_AS char*)(const LDS_AS void*)base + off);
-}
-
-// s_waitcnt with vmcnt = vm (clamped to the 6-bit field) and lgkmcnt = 0.
-template <int VM>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  constexpr int v = VM > 63 ? 63 : VM;
-  __builtin_amdgcn_s_waitcnt((v & 0xF) | ((v >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
-}
-
-// Workgroup barrier that orders LDS traffic but does not drain outstanding
-// direct-to-LDS gathers (a __syncthreads fence would wait for every one).
-// Callers wait for their own loads first.
-__device__ __forceinline__ void barrier_no_vm_drain() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).  Every
-// register array below is indexed with constants only, which keeps it out of
-// scratch memory regardless of the unroller's size limits.
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// Keep an MFMA accumulator tile in AGPRs at a non-MFMA definition or use, so
-// that its whole live range stays in the accumulator register file.
-__device__ __forceinline__ f32x4 pin_agpr(f32x4 t) {
-  asm volatile("" : "+a"(t));
-  return t;
-}
-
-__device__ __forceinline__ float wave_max16x4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
 
 // Compact the valid slots of [lo, hi) of one token's index row into sidx,
 // in order.  Returns the number of valid slots.  All threads participate.
@@ -859,109 +779,43 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   write_output<SPLIT>(a, st, token, split, head, g, nvalid);
 }
 
-// Log-sum-exp merge of split partials: one thread per (token, head, 8 columns).
-__global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.s_q * a.h_q * (kDv / 8);
-  if (t >= total) return;
-  const int q8 = (int)(t % (kDv / 8));
-  const int64_t th = t / (kDv / 8);
-  const int head = (int)(th % a.h_q);
-  const int64_t token = th / a.h_q;
-  const int ns = a.num_splits;
-  const int64_t part0 = token * ns * a.h_q + head;
-  float m = kNegInf;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, a.ws_lse[part0 + (int64_t)s * a.h_q]);
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  float z = 0.f;
-  if (m != kNegInf) {
-    for (int s = 0; s < ns; ++s) {
-      const int64_t part = part0 + (int64_t)s * a.h_q;
-      const float ls = a.ws_lse[part];
-      if (ls == kNegInf) continue;
-      const float wgt = __expf(ls - m);
-      z += wgt;
-      const f32x4* src = (const f32x4*)(a.ws_o + part * kDv + 8 * q8);
-      acc0 += wgt * src[0];
-      acc1 += wgt * src[1];
-    }
-  }
-  const float inv = z > 0.f ? 1.0f / z : 0.f;
-  i32x4 v;
-  v[0] = (int)pack2_bf16(acc0[0] * inv, acc0[1] * inv);
-  v[1] = (int)pack2_bf16(acc0[2] * inv, acc0[3] * inv);
-  v[2] = (int)pack2_bf16(acc1[0] * inv, acc1[1] * inv);
-  v[3] = (int)pack2_bf16(acc1[2] * inv, acc1[3] * inv);
-  *(i32x4*)(a.out + token * a.out_st + (int64_t)head * a.out_sh + 8 * q8) = v;
-  if (q8 == 0) a.lse[token * a.lse_st + head] = z > 0.f ? m + __logf(z) : kNegInf;
-}
-
 unsigned grid_size(const FwdArgs& a) {
   const int64_t items = (int64_t)a.s_q * a.num_splits;
   if (a.head_groups == 1) return (unsigned)items;
   return (unsigned)(((items + 7) / 8) * 8 * a.head_groups);
 }
 
-template <int NW, int BT, bool SPLIT>
-hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
+template <int NW, int BT, bool SPLIT, bool BUF>
+void launch_bf16_variant(const FwdArgs& a, hipStream_t stream) {
   constexpr int NST = BT == 32 ? 4 : 2;
-  const unsigned grid = grid_size(a);
-  if (a.kv_window_bytes)
-    hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, true>), dim3(grid), dim3(NW * 64), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, false>), dim3(grid), dim3(NW * 64), 0,
-                       stream, a);
-  return hipGetLastError();
+  hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, BUF>), dim3(grid_size(a)), dim3(NW * 64),
+                     0, stream, a);
 }
 
-template <int NW>
-hipError_t launch_nw(const FwdArgs& a, int b_topk, hipStream_t stream) {
-  const bool split = a.num_splits > 1;
-  if (b_topk == 64) return split ? launch_bf16<NW, 64, true>(a, stream) : launch_bf16<NW, 64, false>(a, stream);
-  return split ? launch_bf16<NW, 32, true>(a, stream) : launch_bf16<NW, 32, false>(a, stream);
+template <int NW, bool SPLIT, bool BUF>
+void launch_fp8_variant(const FwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, SPLIT, BUF>), dim3(grid_size(a)), dim3(NW * 64), 0, stream, a);
 }
 
 }  // namespace
 
-template <int NW, bool BUF>
-hipError_t launch_fp8_src(const FwdArgs& a, hipStream_t stream) {
-  const unsigned grid = grid_size(a);
-  if (a.num_splits > 1)
-    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, true, BUF>), dim3(grid), dim3(NW * 64), 0, stream, a);
+template <int NW, int BT>
+hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
+  const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
+  if (split)
+    buf ? launch_bf16_variant<NW, BT, true, true>(a, stream) : launch_bf16_variant<NW, BT, true, false>(a, stream);
   else
-    hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, false, BUF>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    buf ? launch_bf16_variant<NW, BT, false, true>(a, stream) : launch_bf16_variant<NW, BT, false, false>(a, stream);
   return hipGetLastError();
 }
 
 template <int NW>
 hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
-  return a.kv_window_bytes ? launch_fp8_src<NW, true>(a, stream) : launch_fp8_src<NW, false>(a, stream);
-}
-
-hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream) {
-  hipError_t e;
-  if (fp8) {
-    switch (a.h_q) {
-      case 16: e = launch_fp8<1>(a, stream); break;
-      case 32: e = launch_fp8<2>(a, stream); break;
-      case 64:
-      case 128: e = launch_fp8<4>(a, stream); break;   // 128: two head groups
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (a.h_q) {
-      case 16: e = launch_nw<1>(a, b_topk, stream); break;
-      case 32: e = launch_nw<2>(a, b_topk, stream); break;
-      case 64:
-      case 128: e = launch_nw<4>(a, b_topk, stream); break;   // 128: two head groups
-      default: return hipErrorInvalidValue;
-    }
-  }
-  if (e != hipSuccess || a.num_splits <= 1) return e;
-  const int64_t threads = (int64_t)a.s_q * a.h_q * (kDv / 8);
-  hipLaunchKernelGGL(smla_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, a);
+  const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
+  if (split)
+    buf ? launch_fp8_variant<NW, true, true>(a, stream) : launch_fp8_variant<NW, true, false>(a, stream);
+  else
+    buf ? launch_fp8_variant<NW, false, true>(a, stream) : launch_fp8_variant<NW, false, false>(a, stream);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI layer (smla_api.cpp) and the gfx950
-// kernels (smla_kernels.hip).  Not installed, not part of the ABI.
+// kernels (smla_fwd.cuh, instantiated by the smla_fwd_*.hip units; dispatch in
+// smla_launch.hip).  Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -44,5 +45,13 @@ struct FwdArgs {
 // fp8 selects the packed-fp8 KV producer.  Returns the HIP error of the
 // launches.
 hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream);
+
+// Forward kernel launchers per configuration (NW = waves per workgroup =
+// heads per workgroup / 16; BT = B_TOPK), each instantiated in its own
+// translation unit.
+template <int NW, int BT>
+hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream);
+template <int NW>
+hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace smla

@@ -1,0 +1,79 @@
+// Host dispatch of the forward pass and the split-topk combine kernel.
+//
+// Combine (page "Ascend Sparse Attention Forward 算法与优化技术简析", section
+// 数学建模: tokens are independent and the softmax over a token's slots can be
+// merged from parts by their log-sum-exp): out = Σ_s e^{lse_s − lse} out_s,
+// lse = log Σ_s e^{lse_s}; an empty part (lse = −∞) has weight 0.
+#include "smla_common.cuh"
+
+namespace smla {
+namespace {
+
+// Log-sum-exp merge of split partials: one thread per (token, head, 8 columns).
+__global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.s_q * a.h_q * (kDv / 8);
+  if (t >= total) return;
+  const int q8 = (int)(t % (kDv / 8));
+  const int64_t th = t / (kDv / 8);
+  const int head = (int)(th % a.h_q);
+  const int64_t token = th / a.h_q;
+  const int ns = a.num_splits;
+  const int64_t part0 = token * ns * a.h_q + head;
+  float m = kNegInf;
+  for (int s = 0; s < ns; ++s) m = fmaxf(m, a.ws_lse[part0 + (int64_t)s * a.h_q]);
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  float z = 0.f;
+  if (m != kNegInf) {
+    for (int s = 0; s < ns; ++s) {
+      const int64_t part = part0 + (int64_t)s * a.h_q;
+      const float ls = a.ws_lse[part];
+      if (ls == kNegInf) continue;
+      const float wgt = __expf(ls - m);
+      z += wgt;
+      const f32x4* src = (const f32x4*)(a.ws_o + part * kDv + 8 * q8);
+      acc0 += wgt * src[0];
+      acc1 += wgt * src[1];
+    }
+  }
+  const float inv = z > 0.f ? 1.0f / z : 0.f;
+  i32x4 v;
+  v[0] = (int)pack2_bf16(acc0[0] * inv, acc0[1] * inv);
+  v[1] = (int)pack2_bf16(acc0[2] * inv, acc0[3] * inv);
+  v[2] = (int)pack2_bf16(acc1[0] * inv, acc1[1] * inv);
+  v[3] = (int)pack2_bf16(acc1[2] * inv, acc1[3] * inv);
+  *(i32x4*)(a.out + token * a.out_st + (int64_t)head * a.out_sh + 8 * q8) = v;
+  if (q8 == 0) a.lse[token * a.lse_st + head] = z > 0.f ? m + __logf(z) : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream) {
+  hipError_t e;
+  const bool b64 = b_topk == 64;
+  if (fp8) {
+    switch (a.h_q) {
+      case 16: e = launch_fp8<1>(a, stream); break;
+      case 32: e = launch_fp8<2>(a, stream); break;
+      case 64:
+      case 128: e = launch_fp8<4>(a, stream); break;   // 128: two head groups
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.h_q) {
+      case 16: e = b64 ? launch_bf16<1, 64>(a, stream) : launch_bf16<1, 32>(a, stream); break;
+      case 32: e = b64 ? launch_bf16<2, 64>(a, stream) : launch_bf16<2, 32>(a, stream); break;
+      case 64:
+      case 128:   // 128: two head groups
+        e = b64 ? launch_bf16<4, 64>(a, stream) : launch_bf16<4, 32>(a, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (e != hipSuccess || a.num_splits <= 1) return e;
+  const int64_t threads = (int64_t)a.s_q * a.h_q * (kDv / 8);
+  hipLaunchKernelGGL(smla_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace smla
