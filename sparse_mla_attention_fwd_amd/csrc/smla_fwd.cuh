@@ -104,7 +104,7 @@ struct KvSource {
 // Gather of one block (BT compacted slots) into an LDS stage.  Unit
 // u = m·(BT/8) + rb is filled by one wave instruction; waves take units
 // u = w, w + NW, ... so that each wave keeps a fixed set of row blocks.  Lane
-// l fills slot l of the unit: row 8rb + l%8, chunk 8m + ((l/8) ^ (rb&1)); its
+// l fills slot l of the unit: row 8rb + l%8, chunk 8m + l/8; its
 // address is one row base plus 128·m.  Padding slots past the valid count
 // hold the token's first valid row: it is finite and the softmax gives those
 // slots weight exactly 0.
@@ -134,7 +134,7 @@ struct GatherPlan {
 #pragma unroll
     for (int j = 0; j < NRB; ++j) {
       const int rb = (w + j * NW) % R;
-      const int c = (l >> 3) ^ (rb & 1);
+      const int c = l >> 3;
       const int row = sidx_blk[8 * rb + (l & 7)];
       if constexpr (BUF)
         voff[j] = (uint32_t)row * (uint32_t)row_bytes + (uint32_t)(c << 4);
@@ -200,24 +200,21 @@ __device__ __forceinline__ LaneOffsets<BT> lane_offsets(int lane) {
   // QK: row block 2kt + n/8, row-in-block n%8, chunk-in-group 4(s&1) + g
 #pragma unroll
   for (int v = 0; v < 2; ++v)
-    o.qk[v] = ((n >> 3) * 64 + unit_slot(4 * v + g, n & 7, n >> 3)) * 16;
+    o.qk[v] = ((n >> 3) * 64 + unit_slot(4 * v + g, n & 7)) * 16;
   // V: row 4g + n/4 -> row block g/2 (+4ks), row-in-block 4(g&1) + n/4;
   //    chunk 2dt + ((n&3)>>1) -> group dt/4, chunk-in-group 2(dt&3) + ((n&3)>>1)
   const int rb = g >> 1, r8 = 4 * (g & 1) + (n >> 2);
 #pragma unroll
   for (int v = 0; v < 4; ++v)
-    o.tr[v] = (rb * 64 + unit_slot(2 * v + ((n & 3) >> 1), r8, rb)) * 16 + (n & 1) * 8;
+    o.tr[v] = (rb * 64 + unit_slot(2 * v + ((n & 3) >> 1), r8)) * 16 + (n & 1) * 8;
   return o;
 }
 
-// One block: QKᵀ, skip-scale online softmax, PV.
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 // One block: QKᵀ, skip-scale online softmax, PV.  The LDS operands of both
-// products are fetched PF MFMAs ahead through a small rotating register
-// buffer (scheduling fences keep the order).  With REFILL the gather
-// instructions of a later block are interleaved with the PV MFMAs; with SIDE
-// the side work (the fp8 dequantisation of the next block) is interleaved with
-// the QK MFMAs.
+// products are fetched ahead through small rotating register buffers
+// (scheduling fences keep the order).  With REFILL the gather instructions of
+// a later block are interleaved with the PV MFMAs; with SIDE the side work
+// (the fp8 dequantisation of the next block) is interleaved with the QK MFMAs.
 // No side work in the QK loop (bf16 KV).
 struct NoSideWork {
   static constexpr int PER_THREAD = 0;
@@ -233,9 +230,9 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   constexpr int KT = BT / 16;
   constexpr int UNIT_GROUP = (BT / 8) * 1024;   // bytes between chunk groups
   constexpr int NQ = 18 * KT;                   // QK MFMAs
-  // operand prefetch depth in MFMAs; 512-thread workgroups have 256 registers
-  // per lane and cannot afford a deep buffer
-  constexpr int PF = NW >= 8 ? 2 : 8;
+  // K operand reads in flight (LDS latency under load is ~10 MFMAs; at most
+  // 15 LDS operations can be outstanding per wave)
+  constexpr int PF = FP8 ? 8 : 12;
   const int g = lane >> 4;
 
   // ---- Pᵀ = G·Qᵀ over d_qk = 576 = 18 steps of 32.  MFMA i: step s = i / KT,
@@ -246,6 +243,21 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   auto qk_off = [&](int i) __attribute__((always_inline)) {
     const int s = i / KT, kt = i % KT;
     return lo.qk[s & 1] + (s >> 1) * UNIT_GROUP + kt * 2048;
+  };
+  // Gather instructions of the refill: spread evenly over the MFMAs of both
+  // products (bf16) or of the PV product (fp8, whose QK loop carries the
+  // dequantisation): gathers [ceil(c·NDMA/N), ceil((c+1)·NDMA/N)) follow MFMA
+  // c of the N that carry them.  Issuing them in a burst stalls the wave on a
+  // full vector-memory queue.
+  constexpr int NDMA = Gather::PER_WAVE;
+  constexpr int NPVT = 32 * (BT / 32);          // PV MFMAs
+  constexpr int NQD = SIDE ? 0 : NQ;            // QK MFMAs that carry gathers
+  constexpr int NDT = NQD + NPVT;
+  auto refill_at = [&](auto C) __attribute__((always_inline)) {
+    constexpr int c = decltype(C)::value;
+    if constexpr (REFILL)
+      static_for<(c * NDMA + NDT - 1) / NDT, ((c + 1) * NDMA + NDT - 1) / NDT>(
+          [&](auto K) __attribute__((always_inline)) { next.issue(decltype(K)::value); });
   };
   constexpr int NACC = FP8 ? 5 : 2;
   auto acc_of = [](int s) constexpr { return FP8 ? s / 4 : (s & 1); };
@@ -264,6 +276,7 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
     pacc[acc_of(s)][kt] =
         __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], pacc[acc_of(s)][kt], 0, 0, 0);
     if constexpr (i + PF < NQ) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
+    if constexpr (!SIDE) refill_at(I);
     if constexpr (SIDE) {
       // side tasks [ceil(i·NS/NQ), ceil((i+1)·NS/NQ)) go after MFMA i
       constexpr int NS = Side::PER_THREAD;
@@ -343,18 +356,16 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
 
   // ---- Oᵀ += Vᵀ·Sᵀ, 32 keys per MFMA step.  Lane (g, n) holds S for head n
   // and keys {32ks + 4g + e, 32ks + 16 + 4g + e}, e < 4; the transposed reads
-  // give the V operand the same key order.  MFMA i: ks = i / 32, dt = i % 32.
-  constexpr int NPV = 32 * (BT / 32);
-  constexpr int PFV = NW >= 8 ? 2 : 4;
-  constexpr int NDMA = Gather::PER_WAVE;
+  // give the V operand the same key order.
+  constexpr int KS = BT / 32;                   // key steps of 32
   // S as the bf16 B operand; fp8 KV: one operand per 128-column V group with
   // that row's group scale folded in, so that the V operand stays the exact code.
   constexpr int NSB = FP8 ? 4 : 1;
-  bf16x8 sb[NSB][BT / 32];
+  bf16x8 sb[NSB][KS];
 #pragma unroll
   for (int gv = 0; gv < NSB; ++gv) {
 #pragma unroll
-    for (int ks = 0; ks < BT / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       float w[2][4];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -369,13 +380,17 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
       sb[gv][ks] = t.v;
     }
   }
-  auto tr_off = [&](int i) __attribute__((always_inline)) {
-    const int ks = i / 32, dt = i % 32;
-    return lo.tr[dt & 3] + (dt >> 2) * UNIT_GROUP + ks * 4096;
-  };
   auto tr_load = [&](int off) __attribute__((always_inline)) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off));
+  };
+  // Every wave multiplies its own 16 heads with the whole V tile.
+  // MFMA i: ks = i / 32, dv tile dt = i % 32.
+  constexpr int NPV = 32 * KS;
+  constexpr int PFV = 6;                      // V fragments (2 reads each) in flight
+  auto tr_off = [&](int i) __attribute__((always_inline)) {
+    const int ks = i / 32, dt = i % 32;
+    return lo.tr[dt & 3] + (dt >> 2) * UNIT_GROUP + ks * 4096;
   };
   i16x4 va[PFV], vb[PFV];
 #pragma unroll
@@ -395,12 +410,7 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
       va[i % PFV] = tr_load(tr_off(i + PFV));
       vb[i % PFV] = tr_load(tr_off(i + PFV) + 2048);
     }
-    // gather instructions [ceil(i·NDMA/NPV), ceil((i+1)·NDMA/NPV)) go after MFMA i:
-    // all NDMA of them, spread evenly over the NPV MFMAs
-    if constexpr (REFILL) {
-      static_for<(i * NDMA + NPV - 1) / NPV, ((i + 1) * NDMA + NPV - 1) / NPV>(
-          [&](auto K) __attribute__((always_inline)) { next.issue(decltype(K)::value); });
-    }
+    refill_at(std::integral_constant<int, NQD + decltype(I)::value>{});
     __builtin_amdgcn_sched_barrier(0);
   });
 }
@@ -449,9 +459,7 @@ __device__ __forceinline__ void init_state(State& st) {
 template <bool SPLIT>
 __device__ __forceinline__ void write_output(const FwdArgs& a, State& st, int token, int split,
                                              int head, int g, int nvalid) {
-  float l = st.sumexp;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  const float l = wave_sum16x4(st.sumexp);
   const bool empty = nvalid == 0;
   const float inv = empty ? 0.f : 1.0f / l;
   const float lse = empty ? kNegInf : (st.running_max_for_softmax + __builtin_amdgcn_logf(l)) * kLn2;
@@ -665,7 +673,7 @@ struct DequantFp8 {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int ch = 2 * cc + h;
-      const int off = ((ch >> 3) * (BT / 8) + rb) * 1024 + unit_slot(ch & 7, r8, rb) * 16;
+      const int off = ((ch >> 3) * (BT / 8) + rb) * 1024 + unit_slot(ch & 7, r8) * 16;
       *(LDS_AS i32x4*)((LDS_AS char*)(LDS_AS void*)tile + off) =
           i32x4{(int)o[4 * h], (int)o[4 * h + 1], (int)o[4 * h + 2], (int)o[4 * h + 3]};
     }
