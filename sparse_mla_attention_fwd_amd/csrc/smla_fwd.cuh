@@ -807,24 +807,4 @@ void launch_fp8_variant(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-template <int NW, int BT>
-hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
-  const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
-  if (split)
-    buf ? launch_bf16_variant<NW, BT, true, true>(a, stream) : launch_bf16_variant<NW, BT, true, false>(a, stream);
-  else
-    buf ? launch_bf16_variant<NW, BT, false, true>(a, stream) : launch_bf16_variant<NW, BT, false, false>(a, stream);
-  return hipGetLastError();
-}
-
-template <int NW>
-hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
-  const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
-  if (split)
-    buf ? launch_fp8_variant<NW, true, true>(a, stream) : launch_fp8_variant<NW, true, false>(a, stream);
-  else
-    buf ? launch_fp8_variant<NW, false, true>(a, stream) : launch_fp8_variant<NW, false, false>(a, stream);
-  return hipGetLastError();
-}
-
 }  // namespace smla

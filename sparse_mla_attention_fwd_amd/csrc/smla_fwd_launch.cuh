@@ -1,0 +1,48 @@
+// Launchers of the forward kernels per configuration (instantiated by the
+// smla_fwd_*.hip units).
+#pragma once
+
+#include "smla_fwd_pipe.cuh"
+
+namespace smla {
+
+// Slots per split from which the pipelined kernel is used.
+constexpr int kPipeMinSlots = 1024;
+
+template <int NW, int BT>
+hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
+  const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
+  if constexpr (NW == 4 && BT == 32) {
+    // 64 heads per workgroup, B_TOPK 32, long splits: the pipelined d_v-split
+    // kernel (its prologue costs more; short decode splits keep the other one)
+    if (a.slots_per_split >= kPipeMinSlots) {
+      const dim3 grid(grid_size(a)), block(256);
+      if (split && buf)
+        hipLaunchKernelGGL((smla_fwd_bf16_pipe_kernel<true, true>), grid, block, 0, stream, a);
+      else if (split)
+        hipLaunchKernelGGL((smla_fwd_bf16_pipe_kernel<true, false>), grid, block, 0, stream, a);
+      else if (buf)
+        hipLaunchKernelGGL((smla_fwd_bf16_pipe_kernel<false, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((smla_fwd_bf16_pipe_kernel<false, false>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  if (split)
+    buf ? launch_bf16_variant<NW, BT, true, true>(a, stream) : launch_bf16_variant<NW, BT, true, false>(a, stream);
+  else
+    buf ? launch_bf16_variant<NW, BT, false, true>(a, stream) : launch_bf16_variant<NW, BT, false, false>(a, stream);
+  return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
+  const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
+  if (split)
+    buf ? launch_fp8_variant<NW, true, true>(a, stream) : launch_fp8_variant<NW, true, false>(a, stream);
+  else
+    buf ? launch_fp8_variant<NW, false, true>(a, stream) : launch_fp8_variant<NW, false, false>(a, stream);
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -1,0 +1,470 @@
+// Software-pipelined forward kernel for 64 heads per workgroup, B_TOPK 32 and
+// bf16 KV (prefill, causal and bf16 decode with h_q 64 or 128).
+//
+// Same method as the kernels in smla_fwd.cuh (page "Ascend Sparse Attention
+// Forward 算法与优化技术简析", sections 数学建模 and 计算流程: gathered rows,
+// P = Q·Gᵀ, block-wise online softmax with the skip-scale rule, S cast to bf16
+// before S·V), scheduled differently:
+//
+//  * d_v split of the PV product.  Wave w computes the QKᵀ scores and the
+//    softmax of its 16 heads, then publishes its block's bf16 S operand and
+//    rescale factors through LDS; every wave multiplies the S of all 64 heads
+//    with its own 128 columns of V.  A V fragment is thus read from LDS once
+//    per workgroup and feeds four MFMAs (instead of every wave reading all of
+//    V for its 16 heads), which cuts the LDS read traffic of a block by 35%.
+//  * One barrier per block, and the block pipeline is skewed by one: in
+//    iteration i a wave runs QKᵀ of block i+1 first (its MFMAs hide the LDS
+//    latency of fetching the published S of block i), then the PV products of
+//    block i with the softmax of block i+1 interleaved between its MFMAs.
+//  * No index compaction in LDS (that room holds the S exchange): each
+//    gathering lane loads its row index from global memory four blocks ahead.
+//    Invalid slots gather the split's first valid row and are masked through
+//    a per-block validity word; blocks past the split's last valid slot are
+//    skipped.
+#pragma once
+
+#include <climits>
+
+#include "smla_fwd.cuh"
+
+namespace smla {
+namespace {
+
+// Scan of one split's slots [lo, hi) by the whole workgroup: blocks up to the
+// last valid slot, the first valid row (the padding row) and the valid count.
+struct SplitScan {
+  int nblk, pad_row, nvalid;
+};
+
+template <int BT, int NT>
+__device__ SplitScan scan_split(const int32_t* __restrict__ irow, int lo, int hi, int64_t s_kv,
+                                int* sred, int tid) {
+  if (tid == 0) {
+    sred[0] = -1;
+    sred[1] = INT_MAX;
+    sred[2] = 0;
+  }
+  // all loads first (a split holds at most kMaxSlotsPerSplit slots)
+  constexpr int PER = kMaxSlotsPerSplit / NT;
+  int v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int j = lo + k * NT + tid;
+    v[k] = j < hi ? irow[j] : -1;
+  }
+  __syncthreads();
+  int last = -1, first = INT_MAX, cnt = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int j = lo + k * NT + tid;
+    if (v[k] >= 0 && (int64_t)v[k] < s_kv) {
+      last = j;
+      first = min(first, j);
+      ++cnt;
+    }
+  }
+  if (cnt) {
+    atomicMax(&sred[0], last);
+    atomicMin(&sred[1], first);
+    atomicAdd(&sred[2], cnt);
+  }
+  __syncthreads();
+  SplitScan s;
+  s.nvalid = sred[2];
+  s.nblk = s.nvalid ? (sred[0] - lo) / BT + 1 : 0;
+  s.pad_row = s.nvalid ? irow[sred[1]] : 0;
+  return s;
+}
+
+// Gather of one row block of one block: the lane's row (row 8w + lane%8 of the
+// block, its 16-byte chunk lane/8 of each 128-byte line) and the nine
+// direct-to-LDS instructions that fill units (k, w), k < 9, of the stage.
+template <bool BUF>
+struct RowGather {
+  uint32_t voff;
+  const char* base;
+  // raw: the slot's index (or -1).  Returns whether the slot is valid.
+  __device__ __forceinline__ bool prepare(const KvSource<BUF>& src, int64_t row_bytes, int raw,
+                                          int pad_row, int64_t s_kv, int lane) {
+    const bool valid = raw >= 0 && (int64_t)raw < s_kv;
+    const int row = valid ? raw : pad_row;
+    const int c = lane >> 3;
+    if constexpr (BUF)
+      voff = (uint32_t)row * (uint32_t)row_bytes + (uint32_t)(c << 4);
+    else
+      base = src.kv + (int64_t)row * row_bytes + (c << 4);
+    return valid;
+  }
+  __device__ __forceinline__ void issue(const KvSource<BUF>& src, char* stage, int w, int k) const {
+    src.load16((LDS_AS void*)(stage + (k * 4 + w) * 1024), voff, base, 128 * k);
+  }
+};
+
+// Register state of a wave: the output tiles of all 64 heads for this wave's
+// 128 columns, and the online-softmax state of its own 16 heads.
+struct PipeState {
+  f32x4 o[32];      // tile ht·8 + j = Oᵀ[dv 16(8w + j) + 4g + r][head 16ht + n]
+  float running_max;
+  float running_max_for_softmax;
+  float sumexp;     // this lane's partial running_sumexp of head n (own tile)
+};
+
+template <bool SPLIT, bool BUF>
+__global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
+  constexpr int NW = 4, BT = 32, KT = 2;
+  constexpr int NQ = 36;                      // QK MFMAs per block
+  constexpr int NPV = 32;                     // PV MFMAs per block (8 V fragments x 4 head tiles)
+  constexpr int LPB = 9;                      // gather instructions per wave per block
+  constexpr int TILE = BT * kRowBytesBf16;
+  constexpr int UG = (BT / 8) * 1024;         // bytes between chunk groups of a stage
+  constexpr int PF = 12;                      // K operand reads in flight
+  constexpr int PFV = 4;                      // V fragments (two reads each) in flight
+  constexpr int XS = NW * 64 * 16;            // published S operands of one block
+  // Statically distinct LDS objects: the compiler tracks direct-to-LDS writes
+  // per object, so reading one stage never waits for gathers into another.
+  __shared__ __attribute__((aligned(1024))) char st0[TILE];
+  __shared__ __attribute__((aligned(1024))) char st1[TILE];
+  __shared__ __attribute__((aligned(1024))) char st2[TILE];
+  __shared__ __attribute__((aligned(1024))) char st3[TILE];
+  __shared__ __attribute__((aligned(16))) char xs0[XS];
+  __shared__ __attribute__((aligned(16))) char xs1[XS];
+  __shared__ __attribute__((aligned(16))) float xa0[NW * 64];
+  __shared__ __attribute__((aligned(16))) float xa1[NW * 64];
+  __shared__ __attribute__((aligned(16))) uint32_t vmask[4];   // per stage: slot validity bits
+  __shared__ float lsh[NW * 16];
+  __shared__ int sred[4];
+  char* const stages[4] = {st0, st1, st2, st3};
+  char* const xss[2] = {xs0, xs1};
+  float* const xas[2] = {xa0, xa1};
+
+  WorkItem wi;
+  if (!work_item(a, wi)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int lo = wi.split * a.slots_per_split;
+  const int hi = min(a.topk, lo + a.slots_per_split);
+  const int32_t* __restrict__ irow = a.idx + (int64_t)wi.token * a.idx_st;
+  const int head = wi.head0 + w * 16 + n;
+  bf16x8 qf[18];
+  load_q(a, wi.token, head, g, qf);
+  const SplitScan sc = scan_split<BT, NW * 64>(irow, lo, hi, a.s_kv, sred, tid);
+  const int nblk = sc.nblk;
+  PipeState st;
+#pragma unroll
+  for (int t = 0; t < 32; ++t) st.o[t] = pin_agpr(f32x4{0.f, 0.f, 0.f, 0.f});
+  st.running_max = kNegInf;
+  st.running_max_for_softmax = kNegInf;
+  st.sumexp = 0.f;
+  const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
+  const KvSource<BUF> src(a.kv, a.kv_window_bytes);
+  const int wbase = 2 * UG * w;               // this wave's 128 dv columns: chunk groups 2w, 2w+1
+
+  // This lane's gather slot in block b (row 8w + lane%8) and its index, or -1.
+  // The load is never predicated off (its address is clamped into the split,
+  // which is non-empty whenever a block runs): the wait counts below count it.
+  auto load_idx = [&](int b) __attribute__((always_inline)) {
+    const int j = lo + b * BT + 8 * w + (lane & 7);
+    const int v = irow[min(j, hi - 1)];
+    return j < hi ? v : -1;
+  };
+  // Prepare the gather of block b into stage s (publishing its validity bits).
+  auto prepare_gather = [&](RowGather<BUF>& rg, int s, int raw) __attribute__((always_inline)) {
+    const bool valid = rg.prepare(src, a.kv_row_bytes, raw, sc.pad_row, a.s_kv, lane);
+    const uint32_t bits = (uint32_t)__ballot(valid) & 0xFFu;   // lanes 0..7: rows 8w..8w+7
+    if (lane == 0) *((LDS_AS uint8_t*)(LDS_AS void*)vmask + s * 4 + w) = (uint8_t)bits;
+  };
+
+  auto qk_off = [&](int i) __attribute__((always_inline)) {
+    const int s = i / KT, kt = i % KT;
+    return lofs.qk[s & 1] + (s >> 1) * UG + kt * 2048;
+  };
+  auto tr_off = [&](int jj) __attribute__((always_inline)) {
+    return wbase + lofs.tr[jj & 3] + (jj >> 2) * UG;
+  };
+  auto tr_load = [&](const char* tile, int off) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off));
+  };
+
+  // ---- Pᵀ = G·Qᵀ of one block (bf16 MFMA 16x16x32; even and odd d_qk steps
+  // accumulate separately).  hook(i) runs after MFMA i.
+  auto qk = [&](const char* tile, f32x4 (&pacc)[2][KT], auto&& hook) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) pacc[c][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 abuf[PF];
+    static_for<0, PF>([&](auto I) __attribute__((always_inline)) {
+      abuf[decltype(I)::value] = lds_load<bf16x8>(tile, qk_off(decltype(I)::value));
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NQ>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      constexpr int s = i / KT, kt = i % KT;
+      pacc[s & 1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], pacc[s & 1][kt], 0, 0, 0);
+      if constexpr (i + PF < NQ) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
+      hook(I);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- Online softmax of one block in steps (interleaved with PV MFMAs).
+  // Lane (g, n) holds the scores of keys 16kt + 4g + r of head n.
+  struct Soft {
+    float x[KT][4];
+    float cur, alpha;
+    bool any;
+    bf16x8 s;
+  };
+  auto soft_step = [&](auto K, Soft& sm, const f32x4 (&pacc)[2][KT], uint32_t vm) __attribute__((always_inline)) {
+    constexpr int k = decltype(K)::value;
+    if constexpr (k == 0) {
+      // scaled logits in log2 units; invalid slots masked
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = (pacc[0][kt][r] + pacc[1][kt][r]) * a.scale_log2;
+          sm.x[kt][r] = (vm >> (16 * kt + 4 * g + r)) & 1u ? v : kNegInf;
+        }
+      float c = sm.x[0][0];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c = fmaxf(c, sm.x[kt][r]);
+      sm.cur = c;
+    } else if constexpr (k == 1) {
+      sm.cur = wave_max16x4(sm.cur);
+    } else if constexpr (k == 2) {
+      // skip scale: move running_max_for_softmax (and rescale) only when some
+      // head of this wave has run more than RESCALE_THRES past it
+      const float rmax = fmaxf(st.running_max, sm.cur);
+      st.running_max = rmax;
+      const bool trig = rmax - st.running_max_for_softmax > kRescaleThresLog2;
+      sm.any = __ballot(trig) != 0ull;
+      // exp2(-inf) = 0 when nothing was valid before: the zero state stays zero
+      const float al = __builtin_amdgcn_exp2f(st.running_max_for_softmax - rmax);
+      sm.alpha = sm.any && rmax != kNegInf ? al : 1.0f;
+      st.running_max_for_softmax = sm.any ? rmax : st.running_max_for_softmax;
+      st.sumexp *= sm.alpha;
+    } else if constexpr (k == 3 || k == 4) {
+      // exponentials (a masked slot weighs exactly 0, also before any valid slot)
+      constexpr int kt = k - 3;
+      const float m = st.running_max_for_softmax;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float xv = sm.x[kt][r];
+        sm.x[kt][r] = xv == kNegInf ? 0.f : __builtin_amdgcn_exp2f(xv - m);
+      }
+    } else if constexpr (k == 5) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.sumexp += sm.x[kt][r];
+      union { uint32_t u[4]; bf16x8 v; } t;
+      t.u[0] = pack2_bf16(sm.x[0][0], sm.x[0][1]);
+      t.u[1] = pack2_bf16(sm.x[0][2], sm.x[0][3]);
+      t.u[2] = pack2_bf16(sm.x[1][0], sm.x[1][1]);
+      t.u[3] = pack2_bf16(sm.x[1][2], sm.x[1][3]);
+      sm.s = t.v;
+    }
+  };
+  constexpr int NSOFT = 6;
+  // publish S operand and rescale factor of this wave's heads for block b
+  auto publish = [&](const Soft& sm, int p) __attribute__((always_inline)) {
+    *(LDS_AS bf16x8*)((LDS_AS char*)(LDS_AS void*)xss[p] + (w * 64 + lane) * 16) = sm.s;
+    *(LDS_AS float*)((LDS_AS char*)(LDS_AS void*)xas[p] + (w * 64 + lane) * 4) = sm.alpha;
+  };
+
+  // ---- prologue: row indices of blocks 0..3, gathers of blocks 0..2
+  int raw[4] = {-1, -1, -1, -1};
+  if (nblk > 0) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) raw[b] = load_idx(b);
+  }
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    if (b < nblk) {
+      RowGather<BUF> rg;
+      prepare_gather(rg, b, raw[b]);
+#pragma unroll
+      for (int k = 0; k < LPB; ++k) rg.issue(src, stages[b], w, k);
+    }
+  }
+  int raw_next = raw[3];   // index for the gather issued in the next iteration
+  if (nblk > 0) {
+    // block 0: QKᵀ and softmax, published for iteration 0
+    if (nblk > 2) wait_vm_lgkm0<2 * LPB>();
+    else if (nblk > 1) wait_vm_lgkm0<LPB>();
+    else wait_vm_lgkm0<0>();
+    barrier_no_vm_drain();
+    f32x4 pacc[2][KT];
+    qk(st0, pacc, [&](auto) {});
+    const uint32_t vm = lds_load<uint32_t>((const char*)vmask, 0);
+    Soft sm;
+    static_for<0, NSOFT>([&](auto K) __attribute__((always_inline)) { soft_step(K, sm, pacc, vm); });
+    publish(sm, 0);
+  }
+
+  // ---- iteration i: consume S(i); QKᵀ(i+1); PV(i) with softmax(i+1); refill
+  // the stage of block i-1 with block i+3; load the row index of block i+4.
+  // DYN: the tail (runtime checks of which of these exist).
+  auto iteration = [&](auto S, int i, auto DYN_) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value;     // stage of block i
+    constexpr int p = s & 1;                  // exchange buffer of block i
+    constexpr bool DYN = decltype(DYN_)::value;
+    const bool next = DYN ? i + 1 < nblk : true;
+    const bool refill = DYN ? i + 3 < nblk : true;
+    const bool idx = DYN ? i + 4 < nblk : true;
+    // Every wave: gather(i+1) landed (its gathers are older than the index
+    // load and the gathers of iteration i-1) and S(i) written.
+    if constexpr (!DYN) {
+      wait_vm_lgkm0<LPB + 1>();
+    } else {
+      if (i == 0) {
+        if (nblk > 2) wait_vm_lgkm0<LPB>();
+        else wait_vm_lgkm0<0>();
+      } else if (i + 3 < nblk) {
+        wait_vm_lgkm0<LPB + 1>();
+      } else if (i + 2 < nblk) {
+        wait_vm_lgkm0<LPB>();
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+    }
+    barrier_no_vm_drain();
+
+    int raw_new = -1;
+    if (idx) raw_new = load_idx(i + 4);
+    RowGather<BUF> rg;
+    if (refill) prepare_gather(rg, (s + 3) & 3, raw_next);
+    char* const rstage = stages[(s + 3) & 3];
+    // gathers [ceil(c·LPB/N), ceil((c+1)·LPB/N)) follow MFMA c of the N = 68
+    // of both products
+    auto dma_at = [&](auto C) __attribute__((always_inline)) {
+      constexpr int c = decltype(C)::value, N = NQ + NPV;
+      static_for<(c * LPB + N - 1) / N, ((c + 1) * LPB + N - 1) / N>([&](auto K) __attribute__((always_inline)) {
+        if (refill) rg.issue(src, rstage, w, decltype(K)::value);
+      });
+    };
+
+    bf16x8 sop[NW];
+    float alph[NW];
+    uint32_t vm = 0;
+    auto consume_reads = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int ht = 0; ht < NW; ++ht) {
+        sop[ht] = lds_load<bf16x8>(xss[p], (ht * 64 + lane) * 16);
+        alph[ht] = lds_load<float>((const char*)xas[p], (ht * 64 + lane) * 4);
+      }
+      vm = lds_load<uint32_t>((const char*)vmask, ((s + 1) & 3) * 4);
+    };
+    const char* const tile = stages[s];
+    i16x4 va[PFV], vb[PFV];
+    auto fetch_v = [&](int jj) __attribute__((always_inline)) {
+      va[jj % PFV] = tr_load(tile, tr_off(jj));
+      vb[jj % PFV] = tr_load(tile, tr_off(jj) + 2048);
+    };
+
+    f32x4 pacc[2][KT];
+    if (next) {
+      qk(stages[(s + 1) & 3], pacc, [&](auto I) __attribute__((always_inline)) {
+        constexpr int q = decltype(I)::value;
+        if constexpr (q == 0) consume_reads();
+        // first V fragments of PV(i), once few K reads remain in flight
+        if constexpr (q >= NQ - PF && q < NQ - PF + 2 * PFV && (q - (NQ - PF)) % 2 == 0)
+          fetch_v((q - (NQ - PF)) / 2);
+        dma_at(I);
+      });
+    } else {
+      consume_reads();
+#pragma unroll
+      for (int jj = 0; jj < PFV; ++jj) fetch_v(jj);
+    }
+
+    // rescale this wave's columns of the head tiles whose owner rescaled (one
+    // rarely taken branch for all tiles: a factor of 1 leaves a tile as is)
+    if (__ballot(alph[0] != 1.0f || alph[1] != 1.0f || alph[2] != 1.0f || alph[3] != 1.0f) != 0ull) {
+#pragma unroll
+      for (int t = 0; t < 32; ++t) st.o[t] = pin_agpr(pin_agpr(st.o[t]) * alph[t / 8]);
+    }
+
+    // ---- Oᵀ += Vᵀ·Sᵀ for this wave's columns: MFMA c uses V fragment c/4
+    // (dv tile 8w + c/4) and the S of head tile c%4; the softmax of block i+1
+    // runs between the MFMAs.
+    Soft sm;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NPV>([&](auto I) __attribute__((always_inline)) {
+      constexpr int c = decltype(I)::value;
+      constexpr int jj = c / NW, ht = c % NW;
+      union { i16x4 h[2]; bf16x8 v; } av;
+      av.h[0] = va[jj % PFV];
+      av.h[1] = vb[jj % PFV];
+      st.o[ht * 8 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, sop[ht], st.o[ht * 8 + jj], 0, 0, 0);
+      if constexpr (ht == NW - 1 && jj + PFV < 8) fetch_v(jj + PFV);
+      if constexpr (c % 4 == 1 && c / 4 < NSOFT) {
+        if (next) soft_step(std::integral_constant<int, c / 4>{}, sm, pacc, vm);
+      }
+      dma_at(std::integral_constant<int, NQ + c>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (next) publish(sm, p ^ 1);
+    raw_next = raw_new;
+  };
+
+  using T = std::integral_constant<bool, true>;
+  using F = std::integral_constant<bool, false>;
+  int i0 = 0;
+  if (nblk > 0) {
+    iteration(std::integral_constant<int, 0>{}, 0, T{});
+    i0 = 1;
+    // steady state: every iteration has a next block, a refill and an index load
+    for (; i0 + 7 < nblk; i0 += 4) {
+      iteration(std::integral_constant<int, 1>{}, i0, F{});
+      iteration(std::integral_constant<int, 2>{}, i0 + 1, F{});
+      iteration(std::integral_constant<int, 3>{}, i0 + 2, F{});
+      iteration(std::integral_constant<int, 0>{}, i0 + 3, F{});
+    }
+    for (; i0 < nblk; i0 += 4) {
+      if (i0 < nblk) iteration(std::integral_constant<int, 1>{}, i0, T{});
+      if (i0 + 1 < nblk) iteration(std::integral_constant<int, 2>{}, i0 + 1, T{});
+      if (i0 + 2 < nblk) iteration(std::integral_constant<int, 3>{}, i0 + 2, T{});
+      if (i0 + 3 < nblk) iteration(std::integral_constant<int, 0>{}, i0 + 3, T{});
+    }
+  }
+
+  // ---- epilogue: every head's running_sumexp from its owner wave; this wave
+  // writes its 128 columns of all 64 heads.
+  const float l = wave_sum16x4(st.sumexp);
+  const bool empty = sc.nvalid == 0;
+  const float lse = empty ? kNegInf : (st.running_max_for_softmax + __builtin_amdgcn_logf(l)) * kLn2;
+  if (g == 0) {
+    lsh[w * 16 + n] = l;
+    if constexpr (!SPLIT)
+      a.lse[(int64_t)wi.token * a.lse_st + head] = lse;
+    else
+      a.ws_lse[((int64_t)wi.token * a.num_splits + wi.split) * a.h_q + head] = lse;
+  }
+  __syncthreads();
+  float inv[NW];
+#pragma unroll
+  for (int ht = 0; ht < NW; ++ht) inv[ht] = empty ? 0.f : 1.0f / lsh[ht * 16 + n];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int ht = t / 8, dt = 8 * w + t % 8;
+    const int hd = wi.head0 + ht * 16 + n;
+    const f32x4 o = pin_agpr(st.o[t]) * inv[ht];
+    if constexpr (!SPLIT) {
+      i32x2 v;
+      v[0] = (int)pack2_bf16(o[0], o[1]);
+      v[1] = (int)pack2_bf16(o[2], o[3]);
+      *(i32x2*)(a.out + (int64_t)wi.token * a.out_st + (int64_t)hd * a.out_sh + 16 * dt + 4 * g) = v;
+    } else {
+      const int64_t part = ((int64_t)wi.token * a.num_splits + wi.split) * a.h_q + hd;
+      *(f32x4*)(a.ws_o + part * kDv + 16 * dt + 4 * g) = o;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace smla

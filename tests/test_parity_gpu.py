@@ -263,3 +263,62 @@ def test_decode_fp8_full_size_sampled(dev):
 def test_decode_full_size_all_tokens(dev):
     x = workloads.make_inputs("decode")
     _sampled(dev, x, np.arange(64), num_splits=4)
+
+
+# ---- long splits (>= 1024 slots, 64 heads per workgroup): the pipelined kernel
+
+
+@pytest.mark.parametrize("h_q", [64, 128])
+@pytest.mark.parametrize("topk,num_splits", [(1024, 1), (1100, 1), (2048, 1), (2048, 2)])
+def test_long_split_cases(dev, h_q, topk, num_splits):
+    x = workloads.make_random(s_q=6, h_q=h_q, topk=topk, s_kv=5000, seed=topk + h_q + num_splits,
+                              invalid_frac=0.2, dup_frac=0.05, q_mult=4.0)
+    idx = x["indices"]
+    idx[1, :] = -1                           # no valid slot
+    idx[2, :700] = -1                        # leading blocks without a valid slot
+    idx[3, :topk - 1] = 10 ** 6              # only the last slot valid
+    idx[4, 40:] = -1                         # trailing blocks skipped
+    out, lse = run_gpu(dev, x, num_splits=num_splits)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"long h{h_q} topk={topk} splits={num_splits}")
+
+
+def test_long_split_unreferenced_rows_are_never_read(dev):
+    """Invalid slots gather a padding row; it must be a referenced one."""
+    x = workloads.make_random(s_q=4, h_q=64, topk=1024, s_kv=6000, seed=21, invalid_frac=0.4)
+    x["indices"][2, :600] = -1
+    idx = x["indices"].numpy()
+    used = np.zeros(6000, dtype=bool)
+    used[idx[(idx >= 0) & (idx < 6000)]] = True
+    kv = x["kv"].clone()
+    kv[torch.from_numpy(~used)] = float("nan")
+    out, lse = run_gpu(dev, dict(x, kv=kv))
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, "long poisoned")
+
+
+@pytest.mark.parametrize("topk", [300, 2048])
+def test_kv_beyond_32bit_offsets(dev, topk):
+    """A bf16 KV of 4.2 M rows (4.8 GB) no longer fits 32-bit byte offsets:
+    the gathers take 64-bit addresses.  Indices span the whole table."""
+    device, smla = dev
+    s_kv = 4_200_000
+    x = workloads.make_random(s_q=3, h_q=64, topk=topk, s_kv=1, seed=31)
+    rng = np.random.default_rng(32)
+    idx = np.stack([rng.choice(s_kv, topk, replace=False) for _ in range(3)])
+    idx[0, :5] = s_kv - 1 - np.arange(5)     # the last rows
+    idx[1, 7] = -1
+    rows = np.unique(idx[idx >= 0])
+    sub = torch.from_numpy(rng.standard_normal((rows.size, 576)).astype(np.float32)).to(torch.bfloat16)
+    kv = torch.zeros((s_kv, 576), dtype=torch.bfloat16, device=device)
+    kv[torch.from_numpy(rows).to(device)] = sub.to(device)
+    q = x["q"].to(device)
+    out, lse = smla.sparse_mla_fwd(q, kv, torch.from_numpy(idx.astype(np.int32)).to(device), x["sm_scale"])
+    torch.cuda.synchronize()
+    remap = np.full(idx.shape, -1, dtype=np.int64)
+    ok = idx >= 0
+    remap[ok] = np.searchsorted(rows, idx[ok])
+    ro, rl = sparse_mla_fwd_exact(workloads.to_f64(x["q"]), workloads.to_f64(sub), remap, x["sm_scale"], 512)
+    del kv
+    torch.cuda.empty_cache()
+    check(out.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64), ro, rl, f"kv 4.8 GB topk={topk}")
