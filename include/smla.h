@@ -122,8 +122,9 @@ typedef struct smla_fwd_params {
   int32_t b_topk;
 
   /* Device scratch for split partial results, needed when the plan has more
-   * than one split; size from smla_fwd_workspace_size.  Caller-owned; it may be
-   * reused by later calls on the same stream. */
+   * than one split; size from smla_fwd_workspace_size (fp32 lse and bf16
+   * normalised output of every part).  Caller-owned; it may be reused by later
+   * calls on the same stream. */
   void* workspace;
   size_t workspace_bytes;
 } smla_fwd_params;

@@ -36,7 +36,9 @@ struct Plan {
 // Decode occupancy: a token's topk range is cut so that the grid holds at least
 // about two workgroups per CU, with no part smaller than 64 slots and none
 // larger than the LDS index buffer.
-constexpr int kTargetWorkgroups = 512;
+// Workgroups a split plan aims for: one per compute unit (the forward kernels
+// hold more than half of a unit's LDS, so one workgroup is resident per unit).
+constexpr int kTargetWorkgroups = 256;
 
 smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   if (!p) return fail(SMLA_ERR_INVALID_ARGUMENT, "params is NULL");
@@ -106,8 +108,9 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   int32_t ns = p->num_splits;
   if (ns == 0) {
     ns = min_splits;
-    if (p->s_q > 0 && (int64_t)p->s_q * ns < kTargetWorkgroups) {
-      const int32_t want = (kTargetWorkgroups + p->s_q - 1) / p->s_q;
+    const int64_t units = (int64_t)p->s_q * (p->h_q > 64 ? p->h_q / 64 : 1);   // workgroups per split
+    if (units > 0 && units * ns < kTargetWorkgroups) {
+      const int32_t want = (int32_t)((kTargetWorkgroups + units - 1) / units);
       const int32_t cap = (p->topk + 63) / 64;   // parts of at least 64 slots
       ns = want < cap ? want : cap;
       if (ns < min_splits) ns = min_splits;
@@ -126,7 +129,7 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   pl.workspace_bytes = 0;
   if (pl.num_splits > 1) {
     const size_t parts = (size_t)p->s_q * pl.num_splits * p->h_q;
-    pl.workspace_bytes = parts * SMLA_D_V * sizeof(float) + ((parts * sizeof(float) + 255) & ~size_t(255));
+    pl.workspace_bytes = parts * SMLA_D_V * sizeof(uint16_t) + ((parts * sizeof(float) + 255) & ~size_t(255));
   }
   *plan = pl;
   return SMLA_OK;
@@ -182,8 +185,8 @@ smla_status smla_fwd(const smla_fwd_params* p, void* stream) {
   if (pl.num_splits > 1) {
     const size_t parts = (size_t)p->s_q * pl.num_splits * p->h_q;
     a.ws_lse = static_cast<float*>(p->workspace);
-    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
-                                      ((parts * sizeof(float) + 255) & ~size_t(255)));
+    a.ws_o = reinterpret_cast<uint16_t*>(static_cast<char*>(p->workspace) +
+                                         ((parts * sizeof(float) + 255) & ~size_t(255)));
   }
   a.s_q = p->s_q;
   a.h_q = p->h_q;

@@ -455,7 +455,7 @@ __device__ __forceinline__ void init_state(State& st) {
 }
 
 // Epilogue: total running_sumexp per head, normalise, write the output (or
-// the split partial: normalised output and lse of this part).
+// the split partial: normalised output, rounded to bf16, and lse of this part).
 template <bool SPLIT>
 __device__ __forceinline__ void write_output(const FwdArgs& a, State& st, int token, int split,
                                              int head, int g, int nvalid) {
@@ -476,9 +476,15 @@ __device__ __forceinline__ void write_output(const FwdArgs& a, State& st, int to
     if (g == 0) a.lse[(int64_t)token * a.lse_st + head] = lse;
   } else {
     const int64_t part = ((int64_t)token * a.num_splits + split) * a.h_q + head;
-    float* orow = a.ws_o + part * kDv + 4 * g;
+    uint16_t* orow = a.ws_o + part * kDv + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(f32x4*)(orow + 16 * dt) = pin_agpr(st.o[dt]) * inv;
+    for (int dt = 0; dt < 32; ++dt) {
+      const f32x4 o = pin_agpr(st.o[dt]);
+      i32x2 v;
+      v[0] = (int)pack2_bf16(o[0] * inv, o[1] * inv);
+      v[1] = (int)pack2_bf16(o[2] * inv, o[3] * inv);
+      *(i32x2*)(orow + 16 * dt) = v;
+    }
     if (g == 0) a.ws_lse[part] = lse;
   }
 }

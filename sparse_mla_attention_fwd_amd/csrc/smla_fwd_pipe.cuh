@@ -454,14 +454,14 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
     const int ht = t / 8, dt = 8 * w + t % 8;
     const int hd = wi.head0 + ht * 16 + n;
     const f32x4 o = pin_agpr(st.o[t]) * inv[ht];
+    i32x2 v;
+    v[0] = (int)pack2_bf16(o[0], o[1]);
+    v[1] = (int)pack2_bf16(o[2], o[3]);
     if constexpr (!SPLIT) {
-      i32x2 v;
-      v[0] = (int)pack2_bf16(o[0], o[1]);
-      v[1] = (int)pack2_bf16(o[2], o[3]);
       *(i32x2*)(a.out + (int64_t)wi.token * a.out_st + (int64_t)hd * a.out_sh + 16 * dt + 4 * g) = v;
     } else {
       const int64_t part = ((int64_t)wi.token * a.num_splits + wi.split) * a.h_q + hd;
-      *(f32x4*)(a.ws_o + part * kDv + 16 * dt + 4 * g) = o;
+      *(i32x2*)(a.ws_o + part * kDv + 16 * dt + 4 * g) = v;
     }
   }
 }

@@ -28,7 +28,7 @@ struct FwdArgs {
   int64_t out_st, out_sh;
   float* lse;
   int64_t lse_st;
-  float* ws_o;              // [s_q, num_splits, h_q, 512] fp32 (split plans)
+  uint16_t* ws_o;           // [s_q, num_splits, h_q, 512] bf16 bits: O/l of each part (split plans)
   float* ws_lse;            // [s_q, num_splits, h_q] fp32 (split plans)
   int32_t s_q, h_q, topk, slots_per_split, num_splits;
   int32_t head_groups;      // workgroups per (token, split): h_q / 64, at least 1

@@ -9,7 +9,8 @@
 namespace smla {
 namespace {
 
-// Log-sum-exp merge of split partials: one thread per (token, head, 8 columns).
+// Log-sum-exp merge of split partials (bf16 O/l and fp32 lse per part): one
+// thread per (token, head, 8 columns).
 __global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.s_q * a.h_q * (kDv / 8);
@@ -31,9 +32,18 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
       if (ls == kNegInf) continue;
       const float wgt = __expf(ls - m);
       z += wgt;
-      const f32x4* src = (const f32x4*)(a.ws_o + part * kDv + 8 * q8);
-      acc0 += wgt * src[0];
-      acc1 += wgt * src[1];
+      // eight bf16 partial values -> fp32 (exact: bf16 is the top half of fp32)
+      const i32x4 pv = *(const i32x4*)(a.ws_o + part * kDv + 8 * q8);
+      f32x4 lo4, hi4;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        lo4[2 * k] = __uint_as_float((uint32_t)pv[k] << 16);
+        lo4[2 * k + 1] = __uint_as_float((uint32_t)pv[k] & 0xFFFF0000u);
+        hi4[2 * k] = __uint_as_float((uint32_t)pv[k + 2] << 16);
+        hi4[2 * k + 1] = __uint_as_float((uint32_t)pv[k + 2] & 0xFFFF0000u);
+      }
+      acc0 += wgt * lo4;
+      acc1 += wgt * hi4;
     }
   }
   const float inv = z > 0.f ? 1.0f / z : 0.f;
