@@ -2,12 +2,14 @@
 // smla_fwd_*.hip units).
 #pragma once
 
-#include "smla_fwd_pipe.cuh"
+#include "smla_fwd_fp8_pipe.cuh"
 
 namespace smla {
 
 // Slots per split from which the pipelined kernel is used.
 constexpr int kPipeMinSlots = 1024;
+// Raw-row stages of the pipelined fp8 kernel.
+constexpr int kFp8Stages = 6;
 
 template <int NW, int BT>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
@@ -38,6 +40,19 @@ hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
 template <int NW>
 hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
   const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
+  if constexpr (NW == 4) {
+    // 64 heads per workgroup: the pipelined kernel with in-register conversion
+    const dim3 grid(grid_size(a)), block(256);
+    if (split && buf)
+      hipLaunchKernelGGL((smla_fwd_fp8_pipe_kernel<true, true, kFp8Stages>), grid, block, 0, stream, a);
+    else if (split)
+      hipLaunchKernelGGL((smla_fwd_fp8_pipe_kernel<true, false, kFp8Stages>), grid, block, 0, stream, a);
+    else if (buf)
+      hipLaunchKernelGGL((smla_fwd_fp8_pipe_kernel<false, true, kFp8Stages>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((smla_fwd_fp8_pipe_kernel<false, false, kFp8Stages>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   if (split)
     buf ? launch_fp8_variant<NW, true, true>(a, stream) : launch_fp8_variant<NW, true, false>(a, stream);
   else

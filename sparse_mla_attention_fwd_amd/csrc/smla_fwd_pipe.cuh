@@ -219,13 +219,14 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
   auto soft_step = [&](auto K, Soft& sm, const f32x4 (&pacc)[2][KT], uint32_t vm) __attribute__((always_inline)) {
     constexpr int k = decltype(K)::value;
     if constexpr (k == 0) {
+      const uint32_t vmg = vm >> (4 * g);   // validity of keys 4g + (16kt + r)
       // scaled logits in log2 units; invalid slots masked
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float v = (pacc[0][kt][r] + pacc[1][kt][r]) * a.scale_log2;
-          sm.x[kt][r] = (vm >> (16 * kt + 4 * g + r)) & 1u ? v : kNegInf;
+          sm.x[kt][r] = (vmg >> (16 * kt + r)) & 1u ? v : kNegInf;
         }
       float c = sm.x[0][0];
 #pragma unroll
