@@ -199,7 +199,7 @@ smla_status smla_fwd(const smla_fwd_params* p, void* stream) {
   {
     const int64_t row_len = p->kv_format == SMLA_KV_BF16 ? 2 * SMLA_D_QK : SMLA_FP8_ROW_BYTES;
     const int64_t window = p->s_kv > 0 ? (p->s_kv - 1) * a.kv_row_bytes + row_len : 0;
-    a.kv_window_bytes = window > 0 && window <= (int64_t)UINT32_MAX ? (uint32_t)window : 0u;
+    a.kv_window_bytes = window > 0 && window <= (int64_t)smla::kDummyOffset ? (uint32_t)window : 0u;
   }
   const hipError_t e = smla::launch_fwd(a, pl.b_topk, p->kv_format == SMLA_KV_FP8_E4M3,
                                         static_cast<hipStream_t>(stream));

@@ -52,6 +52,20 @@ __device__ __forceinline__ T lds_load(const char* base, int off) {
   return *(const LDS_AS T*)((const LDS_AS char*)(const LDS_AS void*)base + off);
 }
 
+// One 32-bit LDS read of byte p + OFF that the compiler cannot see as one: for
+// LDS written by direct-to-LDS loads whose completion the caller's own wait
+// counts already guarantee (the compiler's wait placement would otherwise
+// assume the most recent such load could still be pending).  Waits for the
+// read itself.
+template <int OFF>
+__device__ __forceinline__ int lds_read_opaque(const char* p) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  int v;
+  const uint32_t addr = (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+  asm volatile("ds_read_b32 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return v;
+}
+
 // s_waitcnt with vmcnt = vm (clamped to the 6-bit field) and lgkmcnt = 0.
 template <int VM>
 __device__ __forceinline__ void wait_vm_lgkm0() {

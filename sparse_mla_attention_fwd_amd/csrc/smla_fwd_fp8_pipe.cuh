@@ -65,20 +65,6 @@ __device__ __forceinline__ constexpr int fp8_unit(int m, int rb) {
   return 4 * m + (rb ^ (rb >> 1));
 }
 
-// wait until at most pend (0 .. MAX) younger memory instructions are pending
-template <int MAX>
-__device__ __forceinline__ void wait_vm_upto(int pend) {
-  if constexpr (MAX > 0) {
-    if (pend >= MAX) {
-      wait_vm_lgkm0<MAX>();
-      return;
-    }
-    wait_vm_upto<MAX - 1>(pend);
-  } else {
-    wait_vm_lgkm0<0>();
-  }
-}
-
 template <bool SPLIT, bool BUF, int NST>
 __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
   constexpr int NW = 4, BT = 32, KT = 2;
@@ -100,8 +86,9 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char st5[NST > 5 ? RAW : 16];
   __shared__ __attribute__((aligned(16))) char xs0[XS];
   __shared__ __attribute__((aligned(16))) char xs1[XS];
-  __shared__ __attribute__((aligned(16))) float xa0[NW * 64];
-  __shared__ __attribute__((aligned(16))) float xa1[NW * 64];
+  __shared__ __attribute__((aligned(16))) float xa0[NW * 16];
+  __shared__ __attribute__((aligned(16))) float xa1[NW * 16];
+  __shared__ __attribute__((aligned(16))) int ring[NST][NW * 64];   // index ring (as in the bf16 kernel)
   __shared__ __attribute__((aligned(16))) uint32_t vmask[NST];
   __shared__ float lsh[NW * 16];
   __shared__ int sred[4];
@@ -166,10 +153,20 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
     return fp8_unit(4, R >> 3) * 1024 + (4 * 8 + (R & 7)) * 16;
   };
 
-  auto load_idx = [&](int b) __attribute__((always_inline)) {
+  // Row index of this lane's gather slot in block b (row 8w + lane%8) into
+  // ring slot r by a direct-to-LDS buffer load over the split's index row
+  // (slots past the split read 0 without a memory access); issued in every
+  // iteration, read and tested when the gather is prepared, NST-2 iterations
+  // later.
+  const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc((void*)irow, 0, hi * 4, 0x00020000);
+  auto load_idx = [&](int b, auto R) __attribute__((always_inline)) {
     const int j = lo + b * BT + 8 * w + (lane & 7);
-    const int v = irow[min(j, hi - 1)];
-    return j < hi ? v : -1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, (LDS_AS void*)(&ring[decltype(R)::value][w * 64]), 4,
+                                             (uint32_t)j * 4u, 0, 0, 0);
+  };
+  const char* const ring_lane = (const char*)&ring[0][w * 64 + (lane & 7)];
+  auto read_idx = [&](auto R) __attribute__((always_inline)) {
+    return lds_read_opaque<decltype(R)::value * NW * 64 * 4>(ring_lane);
   };
   // Gather of block b's row block w: 5 instructions, chunk group m of rows
   // 8w + lane%8 (chunk lane/8 of each 128-byte line).
@@ -177,12 +174,13 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
     uint32_t voff;
     const char* base;
   };
-  auto prepare_gather = [&](Gather& gt, int s, int raw) __attribute__((always_inline)) {
-    const bool valid = raw >= 0 && (int64_t)raw < a.s_kv;
+  auto prepare_gather = [&](Gather& gt, int s, int b, int raw) __attribute__((always_inline)) {
+    const int j = lo + b * BT + 8 * w + (lane & 7);
+    const bool valid = j < hi && raw >= 0 && (int64_t)raw < a.s_kv;
     const int row = valid ? raw : sc.pad_row;
     const int c = lane >> 3;
-    if constexpr (BUF)
-      gt.voff = (uint32_t)row * (uint32_t)a.kv_row_bytes + (uint32_t)(c << 4);
+    if constexpr (BUF)   // blocks past the split: dummy loads, dropped by the range check
+      gt.voff = b < nblk ? (uint32_t)row * (uint32_t)a.kv_row_bytes + (uint32_t)(c << 4) : kDummyOffset;
     else
       gt.base = a.kv + (int64_t)row * a.kv_row_bytes + (c << 4);
     const uint32_t bits = (uint32_t)__ballot(valid) & 0xFFu;
@@ -321,7 +319,7 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
         t.u[3] = pack2_bf16(sm.x[1][2] * sc4[1][2][G], sm.x[1][3] * sc4[1][3][G]);
         *(LDS_AS bf16x8*)((LDS_AS char*)(LDS_AS void*)xss[p] + ((G * NW + w) * 64 + lane) * 16) = t.v;
       }
-      *(LDS_AS float*)((LDS_AS char*)(LDS_AS void*)xas[p] + (w * 64 + lane) * 4) = sm.alpha;
+      *(LDS_AS float*)((LDS_AS char*)(LDS_AS void*)xas[p] + (w * 16 + n) * 4) = sm.alpha;   // same in all g
     }
   };
   constexpr int NSOFT = 6;
@@ -332,27 +330,27 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
       for (int r = 0; r < 4; ++r) sc4[kt][r] = lds_load<f32x4>(tile, scale_off(kt, r));
   };
 
-  // ---- prologue: indices of blocks 0..NST-1, gathers of blocks 0..NST-2
-  int raw[NST];
-#pragma unroll
-  for (int b = 0; b < NST; ++b) raw[b] = -1;
+  // ---- prologue: indices of blocks 0..NST-1, gathers of blocks 0..NST-2,
+  // then the indices of blocks NST..2·NST-4.  Ring slot b % NST holds the
+  // indices of block b from their load until its gather is prepared (in
+  // iteration b-NST+1; the load is in iteration b-2·NST+3, before the gathers
+  // that iteration issues, so the wait for those gathers covers it).
+  constexpr int XI = NST - 3;                 // index loads after the prologue gathers
   if (nblk > 0) {
-#pragma unroll
-    for (int b = 0; b < NST; ++b) raw[b] = load_idx(b);
-  }
-#pragma unroll
-  for (int b = 0; b < NST - 1; ++b) {
-    if (b < nblk) {
+    static_for<0, NST>([&](auto B) __attribute__((always_inline)) { load_idx(decltype(B)::value, B); });
+    wait_vm_lgkm0<0>();   // the ring reads below are opaque to the compiler's waits
+    static_for<0, NST - 1>([&](auto B) __attribute__((always_inline)) {   // past the split: dummy loads
+      constexpr int b = decltype(B)::value;
       Gather gt;
-      prepare_gather(gt, b, raw[b]);
+      prepare_gather(gt, b, b, read_idx(B));
 #pragma unroll
       for (int m = 0; m < LPB; ++m) issue(gt, stages[b], m);
-    }
-  }
-  int raw_next = raw[NST - 1];
-  if (nblk > 0) {
+    });
+    static_for<NST, NST + XI>([&](auto B) __attribute__((always_inline)) {
+      load_idx(decltype(B)::value, std::integral_constant<int, decltype(B)::value % NST>{});
+    });
     // block 0: wait for its gathers (the later ones stay in flight)
-    wait_vm_upto<(NST - 2) * LPB>((min(nblk, NST - 1) - 1) * LPB);
+    wait_vm_lgkm0<(NST - 2) * LPB + XI>();
     barrier_no_vm_drain();
     QkOut qo;
     qk(st0, qo, [&](auto) {});
@@ -364,39 +362,33 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
   }
 
   // ---- iteration i: consume S(i); QKᵀ(i+1); PV(i) with softmax(i+1); refill
-  // the stage of block i-1 with block i+NST-1; load the row index of block i+NST.
-  auto iteration = [&](auto S, int i, auto DYN_) __attribute__((always_inline)) {
+  // the stage of block i-1 with block i+NST-1; load the row index of block
+  // i+2·NST-3.
+  auto iteration = [&](auto S, int i, auto FIRST_, auto DYN_) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;     // stage of block i
     constexpr int p = s & 1;                  // exchange buffer of block i (i and s have one parity)
+    constexpr bool FIRST = decltype(FIRST_)::value;   // i = s <= NST-3
     constexpr bool DYN = decltype(DYN_)::value;
     const bool next = DYN ? i + 1 < nblk : true;
-    const bool refill = DYN ? i + NST - 1 < nblk : true;
-    const bool idx = DYN ? i + NST < nblk : true;
-    // gather(i+1) was issued in iteration i-(NST-2) (or in the prologue); after
-    // it came, in each of the iterations i-(NST-3)..i-1, one index load and a
-    // block's gathers (and in the prologue the gathers of the later blocks).
-    if constexpr (!DYN) {
-      wait_vm_lgkm0<(NST - 3) * (LPB + 1)>();
-    } else {
-      int pend = 0;                            // younger memory instructions than gather(i+1)
-      if (i + 1 < nblk) {
-        for (int j = max(i - (NST - 3), 0); j <= i - 1; ++j)
-          pend += (j + NST < nblk ? 1 : 0) + (j + NST - 1 < nblk ? LPB : 0);
-        for (int b = i + 2; b < NST - 1 && b < nblk; ++b) pend += LPB;
-      }
-      wait_vm_upto<(NST - 2) * (LPB + 1)>(pend);
-    }
+    // Every iteration issues the same memory instructions (loads for blocks
+    // past the split are dummies), so the wait counts are constants.
+    // gather(i+1) was issued in iteration i-(NST-2), or for a first iteration
+    // in the prologue; younger are, in each of the iterations i-(NST-3)..i-1,
+    // an index load and a block's gathers, and for a first iteration the
+    // prologue's later gathers and XI index loads: (NST-3)·(LPB+1) + i.
+    wait_vm_lgkm0<(NST - 3) * (LPB + 1) + (FIRST ? s : 0)>();
     barrier_no_vm_drain();
 
-    int raw_new = -1;
-    if (idx) raw_new = load_idx(i + NST);
+    // block i+2·NST-3 takes the ring slot of block i+NST-3 (prepared in
+    // iteration i-2); block i+NST-1's index was loaded in iteration i-NST+2
+    load_idx(i + 2 * NST - 3, std::integral_constant<int, (s + NST - 3) % NST>{});
     Gather gt;
     constexpr int rs = (s + NST - 1) % NST;   // stage of block i-1 = stage of block i+NST-1
-    if (refill) prepare_gather(gt, rs, raw_next);
+    prepare_gather(gt, rs, i + NST - 1, read_idx(std::integral_constant<int, (s + NST - 1) % NST>{}));
     auto dma_at = [&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value, N = NQ + NPV;
       static_for<(c * LPB + N - 1) / N, ((c + 1) * LPB + N - 1) / N>([&](auto K) __attribute__((always_inline)) {
-        if (refill) issue(gt, stages[rs], decltype(K)::value);
+        issue(gt, stages[rs], decltype(K)::value);
       });
     };
 
@@ -409,7 +401,7 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
 #pragma unroll
       for (int ht = 0; ht < NW; ++ht) {
         sop[ht] = lds_load<bf16x8>(xss[p], ((w * NW + ht) * 64 + lane) * 16);
-        alph[ht] = lds_load<float>((const char*)xas[p], (ht * 64 + lane) * 4);
+        alph[ht] = lds_load<float>((const char*)xas[p], (ht * 16 + n) * 4);
       }
       vm = lds_load<uint32_t>((const char*)vmask, sn * 4);
     };
@@ -432,6 +424,9 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
       consume_reads();
 #pragma unroll
       for (int jj = 0; jj < PFV; ++jj) fetch_v(jj);
+      // the gathers the QKᵀ MFMAs would have carried (both paths issue the same
+      // memory instructions)
+      static_for<0, NQ>([&](auto I) __attribute__((always_inline)) { dma_at(I); });
     }
 
     if (__ballot(alph[0] != 1.0f || alph[1] != 1.0f || alph[2] != 1.0f || alph[3] != 1.0f) != 0ull) {
@@ -461,30 +456,44 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
       dma_at(std::integral_constant<int, NQ + c>{});
       __builtin_amdgcn_sched_barrier(0);
     });
-    raw_next = raw_new;
   };
 
   using T = std::integral_constant<bool, true>;
   using F = std::integral_constant<bool, false>;
-  int i0 = NST - 2;
-  if (nblk > 0) {
-    // iterations 0..NST-3 still count prologue gathers: runtime wait counts
-    static_for<0, NST - 2>([&](auto K) __attribute__((always_inline)) {
-      if (decltype(K)::value < nblk) iteration(K, decltype(K)::value, T{});
-    });
-    // steady state: groups of NST iterations keep every stage index a constant
-    for (; i0 + 2 * NST - 1 < nblk; i0 += NST) {
-      static_for<0, NST>([&](auto K) __attribute__((always_inline)) {
-        iteration(std::integral_constant<int, (NST - 2 + decltype(K)::value) % NST>{}, i0 + decltype(K)::value, F{});
-      });
+  // Iterations that may not run are nested, so that each is reached only from
+  // the one before it (the compiler's own waits then see every memory
+  // instruction of the earlier iterations): the first NST-2 iterations, then
+  // (inside the last of them) the steady groups and the last blocks.
+  auto tail = [&](auto self, auto K, int i0) __attribute__((always_inline)) {
+    constexpr int k = decltype(K)::value;
+    if constexpr (k < NST) {
+      if (i0 + k < nblk) {
+        iteration(std::integral_constant<int, (NST - 2 + k) % NST>{}, i0 + k, F{}, T{});
+        self(self, std::integral_constant<int, k + 1>{}, i0);
+      }
     }
-    for (; i0 < nblk; i0 += NST) {
-      static_for<0, NST>([&](auto K) __attribute__((always_inline)) {
-        if (i0 + decltype(K)::value < nblk)
-          iteration(std::integral_constant<int, (NST - 2 + decltype(K)::value) % NST>{}, i0 + decltype(K)::value, T{});
-      });
+  };
+  auto first = [&](auto self, auto K) __attribute__((always_inline)) {
+    constexpr int k = decltype(K)::value;
+    if (k < nblk) {
+      iteration(K, k, T{}, T{});
+      if constexpr (k + 1 < NST - 2) {
+        self(self, std::integral_constant<int, k + 1>{});
+      } else {
+        // steady state: groups of NST iterations keep every stage index a constant
+        int i0 = NST - 2;
+        for (; i0 + NST < nblk; i0 += NST) {
+          static_for<0, NST>([&](auto J) __attribute__((always_inline)) {
+            iteration(std::integral_constant<int, (NST - 2 + decltype(J)::value) % NST>{}, i0 + decltype(J)::value,
+                      F{}, F{});
+          });
+        }
+        tail(tail, std::integral_constant<int, 0>{}, i0);
+      }
     }
-  }
+  };
+  first(first, std::integral_constant<int, 0>{});
+  if (nblk > 0) wait_vm_lgkm0<0>();   // dummy and index loads still in flight
 
   // ---- epilogue (as in the bf16 kernel)
   const float l = wave_sum16x4(st.sumexp);

@@ -16,11 +16,23 @@
 //    iteration i a wave runs QKᵀ of block i+1 first (its MFMAs hide the LDS
 //    latency of fetching the published S of block i), then the PV products of
 //    block i with the softmax of block i+1 interleaved between its MFMAs.
-//  * No index compaction in LDS (that room holds the S exchange): each
-//    gathering lane loads its row index from global memory four blocks ahead.
+//  * No index compaction in LDS (that room holds the S exchange): the row
+//    indices of a block come five blocks ahead, by a direct-to-LDS load per
+//    wave, into a ring of four small LDS slots, and are read and tested when
+//    the block's gather is prepared two iterations later.  Memory wait counts
+//    are in order, so the load is issued early enough that the wait for an
+//    older gather already covers it; holding the indices in LDS (each slot
+//    its own object) rather than in registers keeps the compiler from
+//    placing waits of its own for them.
 //    Invalid slots gather the split's first valid row and are masked through
 //    a per-block validity word; blocks past the split's last valid slot are
 //    skipped.
+//  * Every iteration issues the same memory instructions: the gathers of a
+//    block past the split are dummies (buffer loads outside the KV window,
+//    which the hardware drops; with 64-bit addresses, loads of the padding
+//    row).  All wait counts are then compile-time constants, and the
+//    compiler, whose own waits assume the fewest instructions any path could
+//    have issued, never has to wait for more than the schedule does.
 #pragma once
 
 #include <climits>
@@ -83,14 +95,15 @@ template <bool BUF>
 struct RowGather {
   uint32_t voff;
   const char* base;
-  // raw: the slot's index (or -1).  Returns whether the slot is valid.
+  // raw: the slot's index (or -1); exists: the block lies in the split (else
+  // the loads are dummies).  Returns whether the slot is valid.
   __device__ __forceinline__ bool prepare(const KvSource<BUF>& src, int64_t row_bytes, int raw,
-                                          int pad_row, int64_t s_kv, int lane) {
+                                          int pad_row, int64_t s_kv, int lane, bool exists) {
     const bool valid = raw >= 0 && (int64_t)raw < s_kv;
     const int row = valid ? raw : pad_row;
     const int c = lane >> 3;
     if constexpr (BUF)
-      voff = (uint32_t)row * (uint32_t)row_bytes + (uint32_t)(c << 4);
+      voff = exists ? (uint32_t)row * (uint32_t)row_bytes + (uint32_t)(c << 4) : kDummyOffset;
     else
       base = src.kv + (int64_t)row * row_bytes + (c << 4);
     return valid;
@@ -128,8 +141,11 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char st3[TILE];
   __shared__ __attribute__((aligned(16))) char xs0[XS];
   __shared__ __attribute__((aligned(16))) char xs1[XS];
-  __shared__ __attribute__((aligned(16))) float xa0[NW * 64];
-  __shared__ __attribute__((aligned(16))) float xa1[NW * 64];
+  __shared__ __attribute__((aligned(16))) float xa0[NW * 16];
+  __shared__ __attribute__((aligned(16))) float xa1[NW * 16];
+  // index ring: slot r, lane l of wave w at [r][w·64 + l] holds the index of
+  // its block's row 8w + l%8
+  __shared__ __attribute__((aligned(16))) int ring[4][NW * 64];
   __shared__ __attribute__((aligned(16))) uint32_t vmask[4];   // per stage: slot validity bits
   __shared__ float lsh[NW * 16];
   __shared__ int sred[4];
@@ -160,17 +176,25 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
   const KvSource<BUF> src(a.kv, a.kv_window_bytes);
   const int wbase = 2 * UG * w;               // this wave's 128 dv columns: chunk groups 2w, 2w+1
 
-  // This lane's gather slot in block b (row 8w + lane%8) and its index, or -1.
-  // The load is never predicated off (its address is clamped into the split,
-  // which is non-empty whenever a block runs): the wait counts below count it.
-  auto load_idx = [&](int b) __attribute__((always_inline)) {
+  // Index of this lane's gather slot in block b (row 8w + lane%8) into ring
+  // slot r: a buffer load over the split's index row, so slots past the split
+  // read 0 without a memory access (they are tested against hi when used).
+  // Issued in every iteration, so the wait counts below are exact.
+  const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc((void*)irow, 0, hi * 4, 0x00020000);
+  auto load_idx = [&](int b, auto R) __attribute__((always_inline)) {
     const int j = lo + b * BT + 8 * w + (lane & 7);
-    const int v = irow[min(j, hi - 1)];
-    return j < hi ? v : -1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, (LDS_AS void*)(&ring[decltype(R)::value][w * 64]), 4,
+                                             (uint32_t)j * 4u, 0, 0, 0);
   };
-  // Prepare the gather of block b into stage s (publishing its validity bits).
-  auto prepare_gather = [&](RowGather<BUF>& rg, int s, int raw) __attribute__((always_inline)) {
-    const bool valid = rg.prepare(src, a.kv_row_bytes, raw, sc.pad_row, a.s_kv, lane);
+  const char* const ring_lane = (const char*)&ring[0][w * 64 + (lane & 7)];
+  auto read_idx = [&](auto R) __attribute__((always_inline)) {
+    return lds_read_opaque<decltype(R)::value * NW * 64 * 4>(ring_lane);
+  };
+  // Prepare the gather of block b into stage s from the loaded index raw
+  // (slots past the split are invalid), publishing the validity bits.
+  auto prepare_gather = [&](RowGather<BUF>& rg, int s, int b, int raw) __attribute__((always_inline)) {
+    const int j = lo + b * BT + 8 * w + (lane & 7);
+    const bool valid = rg.prepare(src, a.kv_row_bytes, j < hi ? raw : -1, sc.pad_row, a.s_kv, lane, b < nblk);
     const uint32_t bits = (uint32_t)__ballot(valid) & 0xFFu;   // lanes 0..7: rows 8w..8w+7
     if (lane == 0) *((LDS_AS uint8_t*)(LDS_AS void*)vmask + s * 4 + w) = (uint8_t)bits;
   };
@@ -274,30 +298,25 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
   // publish S operand and rescale factor of this wave's heads for block b
   auto publish = [&](const Soft& sm, int p) __attribute__((always_inline)) {
     *(LDS_AS bf16x8*)((LDS_AS char*)(LDS_AS void*)xss[p] + (w * 64 + lane) * 16) = sm.s;
-    *(LDS_AS float*)((LDS_AS char*)(LDS_AS void*)xas[p] + (w * 64 + lane) * 4) = sm.alpha;
+    *(LDS_AS float*)((LDS_AS char*)(LDS_AS void*)xas[p] + (w * 16 + n) * 4) = sm.alpha;   // same in all g
   };
 
-  // ---- prologue: row indices of blocks 0..3, gathers of blocks 0..2
-  int raw[4] = {-1, -1, -1, -1};
+  // ---- prologue: row indices of blocks 0..3, gathers of blocks 0..2, then
+  // the index of block 4.  Ring slot b % 4 holds the indices of block b from
+  // its load until its gather is prepared.
   if (nblk > 0) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) raw[b] = load_idx(b);
-  }
-#pragma unroll
-  for (int b = 0; b < 3; ++b) {
-    if (b < nblk) {
+    static_for<0, 4>([&](auto B) __attribute__((always_inline)) { load_idx(decltype(B)::value, B); });
+    wait_vm_lgkm0<0>();   // the ring reads below are opaque to the compiler's waits
+    static_for<0, 3>([&](auto B) __attribute__((always_inline)) {
+      constexpr int b = decltype(B)::value;
       RowGather<BUF> rg;
-      prepare_gather(rg, b, raw[b]);
+      prepare_gather(rg, b, b, read_idx(B));
 #pragma unroll
       for (int k = 0; k < LPB; ++k) rg.issue(src, stages[b], w, k);
-    }
-  }
-  int raw_next = raw[3];   // index for the gather issued in the next iteration
-  if (nblk > 0) {
+    });
+    load_idx(4, std::integral_constant<int, 0>{});
     // block 0: QKᵀ and softmax, published for iteration 0
-    if (nblk > 2) wait_vm_lgkm0<2 * LPB>();
-    else if (nblk > 1) wait_vm_lgkm0<LPB>();
-    else wait_vm_lgkm0<0>();
+    wait_vm_lgkm0<2 * LPB + 1>();
     barrier_no_vm_drain();
     f32x4 pacc[2][KT];
     qk(st0, pacc, [&](auto) {});
@@ -308,44 +327,34 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
   }
 
   // ---- iteration i: consume S(i); QKᵀ(i+1); PV(i) with softmax(i+1); refill
-  // the stage of block i-1 with block i+3; load the row index of block i+4.
-  // DYN: the tail (runtime checks of which of these exist).
+  // the stage of block i-1 with block i+3; load the row index of block i+5.
+  // DYN: whether block i+1 exists is checked at run time.
   auto iteration = [&](auto S, int i, auto DYN_) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::value;     // stage of block i
     constexpr int p = s & 1;                  // exchange buffer of block i
     constexpr bool DYN = decltype(DYN_)::value;
     const bool next = DYN ? i + 1 < nblk : true;
-    const bool refill = DYN ? i + 3 < nblk : true;
-    const bool idx = DYN ? i + 4 < nblk : true;
-    // Every wave: gather(i+1) landed (its gathers are older than the index
-    // load and the gathers of iteration i-1) and S(i) written.
-    if constexpr (!DYN) {
-      wait_vm_lgkm0<LPB + 1>();
-    } else {
-      if (i == 0) {
-        if (nblk > 2) wait_vm_lgkm0<LPB>();
-        else wait_vm_lgkm0<0>();
-      } else if (i + 3 < nblk) {
-        wait_vm_lgkm0<LPB + 1>();
-      } else if (i + 2 < nblk) {
-        wait_vm_lgkm0<LPB>();
-      } else {
-        wait_vm_lgkm0<0>();
-      }
-    }
+    // Every wave: gather(i+1) landed and S(i) written.  Younger than
+    // gather(i+1) (issued in iteration i-2, or in the prologue) are the memory
+    // instructions of iteration i-1: an index load and the gathers of block
+    // i+2 (for i = 0 the prologue's gathers of block 2 and index load of
+    // block 4; for i = 1 that index load as well, which this count makes
+    // iteration 1 wait for too: stricter, so also correct).
+    wait_vm_lgkm0<LPB + 1>();
     barrier_no_vm_drain();
 
-    int raw_new = -1;
-    if (idx) raw_new = load_idx(i + 4);
+    // the indices of block i+5 go to the ring slot of block i+1 (prepared in
+    // iteration i-2); block i+3's were loaded in iteration i-2
+    load_idx(i + 5, std::integral_constant<int, (s + 1) & 3>{});
     RowGather<BUF> rg;
-    if (refill) prepare_gather(rg, (s + 3) & 3, raw_next);
+    prepare_gather(rg, (s + 3) & 3, i + 3, read_idx(std::integral_constant<int, (s + 3) & 3>{}));
     char* const rstage = stages[(s + 3) & 3];
     // gathers [ceil(c·LPB/N), ceil((c+1)·LPB/N)) follow MFMA c of the N = 68
     // of both products
     auto dma_at = [&](auto C) __attribute__((always_inline)) {
       constexpr int c = decltype(C)::value, N = NQ + NPV;
       static_for<(c * LPB + N - 1) / N, ((c + 1) * LPB + N - 1) / N>([&](auto K) __attribute__((always_inline)) {
-        if (refill) rg.issue(src, rstage, w, decltype(K)::value);
+        rg.issue(src, rstage, w, decltype(K)::value);
       });
     };
 
@@ -356,7 +365,7 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
 #pragma unroll
       for (int ht = 0; ht < NW; ++ht) {
         sop[ht] = lds_load<bf16x8>(xss[p], (ht * 64 + lane) * 16);
-        alph[ht] = lds_load<float>((const char*)xas[p], (ht * 64 + lane) * 4);
+        alph[ht] = lds_load<float>((const char*)xas[p], (ht * 16 + n) * 4);
       }
       vm = lds_load<uint32_t>((const char*)vmask, ((s + 1) & 3) * 4);
     };
@@ -381,6 +390,9 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
       consume_reads();
 #pragma unroll
       for (int jj = 0; jj < PFV; ++jj) fetch_v(jj);
+      // the gathers the QKᵀ MFMAs would have carried (both paths issue the same
+      // memory instructions)
+      static_for<0, NQ>([&](auto I) __attribute__((always_inline)) { dma_at(I); });
     }
 
     // rescale this wave's columns of the head tiles whose owner rescaled (one
@@ -410,28 +422,33 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     });
     if (next) publish(sm, p ^ 1);
-    raw_next = raw_new;
   };
 
   using T = std::integral_constant<bool, true>;
   using F = std::integral_constant<bool, false>;
-  int i0 = 0;
   if (nblk > 0) {
     iteration(std::integral_constant<int, 0>{}, 0, T{});
-    i0 = 1;
-    // steady state: every iteration has a next block, a refill and an index load
-    for (; i0 + 7 < nblk; i0 += 4) {
+    int i0 = 1;
+    // steady state: every iteration has a next block
+    for (; i0 + 4 < nblk; i0 += 4) {
       iteration(std::integral_constant<int, 1>{}, i0, F{});
       iteration(std::integral_constant<int, 2>{}, i0 + 1, F{});
       iteration(std::integral_constant<int, 3>{}, i0 + 2, F{});
       iteration(std::integral_constant<int, 0>{}, i0 + 3, F{});
     }
-    for (; i0 < nblk; i0 += 4) {
-      if (i0 < nblk) iteration(std::integral_constant<int, 1>{}, i0, T{});
-      if (i0 + 1 < nblk) iteration(std::integral_constant<int, 2>{}, i0 + 1, T{});
-      if (i0 + 2 < nblk) iteration(std::integral_constant<int, 3>{}, i0 + 2, T{});
-      if (i0 + 3 < nblk) iteration(std::integral_constant<int, 0>{}, i0 + 3, T{});
+    // the last blocks (at most four), nested so that an iteration is only
+    // reached from the one before it
+    if (i0 < nblk) {
+      iteration(std::integral_constant<int, 1>{}, i0, T{});
+      if (i0 + 1 < nblk) {
+        iteration(std::integral_constant<int, 2>{}, i0 + 1, T{});
+        if (i0 + 2 < nblk) {
+          iteration(std::integral_constant<int, 3>{}, i0 + 2, T{});
+          if (i0 + 3 < nblk) iteration(std::integral_constant<int, 0>{}, i0 + 3, T{});
+        }
+      }
     }
+    wait_vm_lgkm0<0>();   // dummy and index loads still in flight
   }
 
   // ---- epilogue: every head's running_sumexp from its owner wave; this wave

@@ -15,6 +15,12 @@ constexpr int kFp8RowBytes = 640;         // 576 codes + 5 float32 scales + pad
 constexpr int kMaxSlotsPerSplit = 2048;
 // fp8 KV: the raw-row ring and two bf16 stages leave room for 1536 indices
 constexpr int kMaxSlotsPerSplitFp8 = 1536;
+// Buffer-load offset past every KV window: a gather for a block past the end
+// of a split loads from here, which the hardware drops (range check of the
+// buffer resource), so the load costs no memory traffic.  Windows (last byte
+// of the KV + 1) must not exceed it; the largest instruction offset added to
+// it (1 KB) keeps the sum inside 32 bits.
+constexpr uint32_t kDummyOffset = 0xFFFFF000u;
 
 // Everything one launch of the forward kernel needs, by value.
 struct FwdArgs {
@@ -35,7 +41,7 @@ struct FwdArgs {
   int64_t s_kv;
   float scale_log2;         // sm_scale * log2(e)
   // Bytes of KV reachable with 32-bit offsets from kv: (s_kv - 1) * kv_row_bytes
-  // + the row length when that fits in 32 bits (the gathers then use buffer
+  // + the row length when that is at most kDummyOffset (the gathers then use buffer
   // loads, whose hardware range check also covers every access), else 0 (the
   // gathers use 64-bit global addresses).
   uint32_t kv_window_bytes;
