@@ -424,17 +424,20 @@ struct WorkItem {
   int token, split, head0;
 };
 __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& wi) {
-  const int items = a.s_q * a.num_splits;
-  int item = blockIdx.x, hg = 0;
-  if (a.head_groups > 1) {
-    const int rest = blockIdx.x >> 3;
-    hg = rest % a.head_groups;
-    item = (rest / a.head_groups) * 8 + (blockIdx.x & 7);
-  }
-  if (item >= items) return false;
-  wi.token = item / a.num_splits;
-  wi.split = item - wi.token * a.num_splits;
-  wi.head0 = hg * 64;
+  // The workgroups of one token (head groups x splits) share the token's Q
+  // and, across head groups, its gathered rows.  Workgroup b runs on XCD b % 8
+  // (the dispatcher deals workgroups to the XCDs in turn), so a token's
+  // workgroups take consecutive rounds b / 8 on one XCD: the later ones find
+  // Q and the rows in that XCD's L2.  (A placement hint only: correctness
+  // does not depend on it.)
+  const int per = a.head_groups * a.num_splits;
+  const int b = blockIdx.x, r = b >> 3;
+  const int group = r / per, local = r - group * per;
+  const int token = group * 8 + (b & 7);
+  if (token >= a.s_q) return false;
+  wi.token = token;
+  wi.split = local % a.num_splits;
+  wi.head0 = (local / a.num_splits) * 64;
   return true;
 }
 
@@ -512,6 +515,10 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   const int lo = split * a.slots_per_split;
   const int hi = min(a.topk, lo + a.slots_per_split);
 
+  // Q first: its loads are in flight while the indices are compacted.
+  const int head = wi.head0 + w * 16 + n;
+  bf16x8 qf[18];
+  load_q(a, token, head, g, qf);
   const int nvalid = compact_slots<NW>(a.idx + (int64_t)token * a.idx_st, lo, hi, a.s_kv, sidx,
                                        swcnt, tid);
   const int nblk = (nvalid + BT - 1) / BT;
@@ -519,9 +526,6 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   for (int j = nvalid + tid; j < nblk * BT; j += NW * 64) sidx[j] = sidx[0];
   __syncthreads();
 
-  const int head = wi.head0 + w * 16 + n;
-  bf16x8 qf[18];
-  load_q(a, token, head, g, qf);
   State st;
   init_state(st);
 
@@ -719,15 +723,15 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   const int lo = split * a.slots_per_split;
   const int hi = min(a.topk, lo + a.slots_per_split);
 
+  const int head = wi.head0 + w * 16 + n;
+  bf16x8 qf[18];
+  load_q(a, token, head, g, qf);
   const int nvalid = compact_slots<NW>(a.idx + (int64_t)token * a.idx_st, lo, hi, a.s_kv, sidx,
                                        swcnt, tid);
   const int nblk = (nvalid + BT - 1) / BT;
   for (int j = nvalid + tid; j < nblk * BT; j += NW * 64) sidx[j] = sidx[0];
   __syncthreads();
 
-  const int head = wi.head0 + w * 16 + n;
-  bf16x8 qf[18];
-  load_q(a, token, head, g, qf);
   State st;
   init_state(st);
   const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
@@ -794,9 +798,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
 }
 
 unsigned grid_size(const FwdArgs& a) {
-  const int64_t items = (int64_t)a.s_q * a.num_splits;
-  if (a.head_groups == 1) return (unsigned)items;
-  return (unsigned)(((items + 7) / 8) * 8 * a.head_groups);
+  return (unsigned)(((int64_t)a.s_q + 7) / 8 * 8 * a.head_groups * a.num_splits);
 }
 
 template <int NW, int BT, bool SPLIT, bool BUF>
