@@ -67,5 +67,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+GATHER_CEILING = os.path.join(HERE, "gather_ceiling")
+
+
+def build_gather_ceiling(verbose: bool = False) -> str:
+    """Compile the gather-ceiling measurement program (csrc/gather_ceiling.cpp);
+    returns the path of the executable."""
+    cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-x", "hip", os.path.join(CSRC, "gather_ceiling.cpp"),
+           "-o", GATHER_CEILING + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on gather_ceiling.cpp:\n{r.stderr}")
+    os.replace(GATHER_CEILING + ".tmp", GATHER_CEILING)
+    return GATHER_CEILING
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_gather_ceiling(verbose="-v" in sys.argv))
