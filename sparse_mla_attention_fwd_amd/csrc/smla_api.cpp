@@ -39,6 +39,9 @@ struct Plan {
 // Workgroups a split plan aims for: one per compute unit (the forward kernels
 // hold more than half of a unit's LDS, so one workgroup is resident per unit).
 constexpr int kTargetWorkgroups = 256;
+// Slots the bf16 gather ring of the non-pipelined kernel holds at once (four
+// stages of 32 rows, or two of 64).
+constexpr int32_t kRingSlots = 128;
 
 smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   if (!p) return fail(SMLA_ERR_INVALID_ARGUMENT, "params is NULL");
@@ -194,6 +197,13 @@ smla_status smla_fwd(const smla_fwd_params* p, void* stream) {
   a.slots_per_split = pl.slots_per_split;
   a.num_splits = pl.num_splits;
   a.head_groups = p->h_q > 64 ? p->h_q / 64 : 1;
+  a.inner_groups = 1;
+  if (p->kv_format == SMLA_KV_BF16 && p->h_q > 64 && pl.slots_per_split <= kRingSlots) {
+    // Every block of a split fits in the gather ring at once: one workgroup
+    // gathers the rows once and runs all head groups over them.
+    a.inner_groups = a.head_groups;
+    a.head_groups = 1;
+  }
   a.s_kv = p->s_kv;
   a.scale_log2 = p->sm_scale * 1.4426950408889634f;
   {

@@ -588,7 +588,24 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  write_output<SPLIT>(a, st, token, split, head, g, nvalid);
+  // Further head groups over the same blocks (inner_groups > 1 only when the
+  // split has at most NST blocks: each sits in stage i, complete and visible
+  // since its wait and barrier above, and no refill overwrote it).  The next
+  // group's Q loads are issued before this group's output stores.
+  for (int hg = 1; hg < a.inner_groups; ++hg) {
+    const int prev = head + (hg - 1) * 64;
+    load_q(a, token, head + hg * 64, g, qf);
+    write_output<SPLIT>(a, st, token, split, prev, g, nvalid);
+    init_state(st);
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      if (s < nblk) {
+        GatherPlan<NW, BT, BUF> gp;
+        compute_block<NW, BT, false, false, false>(stages[s], lofs, qf, st, s, nvalid, a.scale_log2, lane, gp, nside);
+      }
+    }
+  }
+  write_output<SPLIT>(a, st, token, split, head + (a.inner_groups - 1) * 64, g, nvalid);
 }
 
 // ---------------------------------------------------------------------------

@@ -38,6 +38,10 @@ struct FwdArgs {
   float* ws_lse;            // [s_q, num_splits, h_q] fp32 (split plans)
   int32_t s_q, h_q, topk, slots_per_split, num_splits;
   int32_t head_groups;      // workgroups per (token, split): h_q / 64, at least 1
+  // Groups of 64 heads that one workgroup runs in turn over the same gathered
+  // blocks (1, or h_q / 64 when every block of a split fits in the stage ring
+  // at once; head_groups is then 1).  bf16 KV, non-pipelined kernel only.
+  int32_t inner_groups;
   int64_t s_kv;
   float scale_log2;         // sm_scale * log2(e)
   // Bytes of KV reachable with 32-bit offsets from kv: (s_kv - 1) * kv_row_bytes

@@ -322,3 +322,38 @@ def test_kv_beyond_32bit_offsets(dev, topk):
     del kv
     torch.cuda.empty_cache()
     check(out.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64), ro, rl, f"kv 4.8 GB topk={topk}")
+
+
+@pytest.mark.parametrize("topk,num_splits,b_topk", [(512, 4, 32), (300, 3, 32), (128, 1, 32),
+                                                    (512, 4, 64), (97, 1, 64), (700, 6, 32)])
+def test_h128_short_splits_one_gather_for_both_head_groups(dev, topk, num_splits, b_topk):
+    """h_q 128 with splits of at most 128 slots: one workgroup gathers a split's
+    rows once and runs both 64-head groups over them.  Ragged last blocks,
+    masked slots, an empty token and a token whose first splits are empty;
+    rows no valid slot names are NaN (a read of one would leak)."""
+    x = workloads.make_random(s_q=6, h_q=128, topk=topk, s_kv=3000, seed=topk + num_splits + b_topk,
+                              invalid_frac=0.3, q_mult=4.0)
+    x["indices"][1, :] = -1
+    x["indices"][2, : topk // 2] = -1
+    idx = x["indices"].numpy()
+    used = np.zeros(3000, dtype=bool)
+    used[idx[(idx >= 0) & (idx < 3000)]] = True
+    kv = x["kv"].clone()
+    kv[torch.from_numpy(~used)] = float("nan")
+    out, lse = run_gpu(dev, dict(x, kv=kv), num_splits=num_splits, b_topk=b_topk)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"h128 topk={topk} ns={num_splits} B{b_topk}")
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+def test_h128_short_splits_one_row_is_bit_exact(dev):
+    x = workloads.make_random(s_q=2, h_q=128, topk=512, s_kv=700, seed=128)
+    rows = [3, 699]
+    for t, r in enumerate(rows):
+        x["indices"][t, :] = r
+    out, lse = run_gpu(dev, x, num_splits=4)
+    for t, r in enumerate(rows):
+        v = x["kv"][r, :512].float().numpy()
+        assert np.array_equal(out[t], np.broadcast_to(v, out[t].shape)), f"row {r} not exact"
+        xr = (workloads.to_f64(x["q"][t]) @ workloads.to_f64(x["kv"][r])) * x["sm_scale"]
+        assert np.abs(lse[t] - (xr + math.log(512))).max() < 1e-4
