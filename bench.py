@@ -63,15 +63,33 @@ def cpu_baseline(x, budget_s: float):
     """Time the float64 oracle on the first tokens of the workload until the
     time budget is used (at least 16 tokens)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    import torch
 
     import workloads
     from oracle import sparse_mla_fwd_exact
 
     w = x["workload"]
-    kv = workloads.to_f64(x["kv"])
     idx = x["indices"].numpy()
     done, t_used, chunk = 0, 0.0, 16
+    if w.page_size:
+        # paged oracle on each token's own pages (float64 copies made outside the timing)
+        from oracle import sparse_mla_fwd_paged
+        ps, table = w.page_size, x["block_table"].numpy()
+        chunk = 2
+        while done < w.s_q and (t_used < budget_s or done < 4):
+            sl = slice(done, min(w.s_q, done + chunk))
+            pages = np.unique(table[sl])
+            rows = torch.from_numpy((pages[:, None] * ps + np.arange(ps)[None, :]).reshape(-1))
+            kv_pages = workloads.to_f64(x["kv"][rows]).reshape(-1, ps, 576)
+            remap = np.searchsorted(pages, table[sl])
+            q = workloads.to_f64(x["q"][sl])
+            t0 = time.perf_counter()
+            sparse_mla_fwd_paged(q, kv_pages, remap, idx[sl], x["sm_scale"], 512)
+            t_used += time.perf_counter() - t0
+            done = sl.stop
+        valid = int((idx[:done] >= 0).sum())
+        return _cpu_result(w, valid, t_used, done, "paged float64 numpy")
+    kv = workloads.to_f64(x["kv"])
     sparse_mla_fwd_exact(workloads.to_f64(x["q"][:1]), kv, idx[:1], x["sm_scale"], 512)  # warm BLAS
     while done < w.s_q and (t_used < budget_s or done < 16):
         sl = slice(done, min(w.s_q, done + chunk))
@@ -81,11 +99,16 @@ def cpu_baseline(x, budget_s: float):
         t_used += time.perf_counter() - t0
         done = sl.stop
     valid = ((idx[:done] >= 0) & (idx[:done] < kv.shape[0])).sum()
+    return _cpu_result(w, valid, t_used, done, "float64 numpy")
+
+
+def _cpu_result(w, valid, t_used, done, kind):
+    from threadpoolctl import threadpool_info
     flops = 2.0 * w.h_q * (576 + 512) * float(valid)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {done} of {w.s_q} tokens of the {w.name} workload, float64 numpy "
+            "sample": f"first {done} of {w.s_q} tokens of the {w.name} workload, {kind} "
                       f"(gather + two GEMMs + exact softmax per token), {t_used:.1f} s"}
 
 
@@ -142,13 +165,21 @@ def main():
                          kv_format=smla.SMLA_KV_FP8_E4M3 if fmt == "fp8" else smla.SMLA_KV_BF16,
                          num_splits=ns, b_topk=args.b_topk)
     plan_splits, plan_bt = smla.smla_fwd_plan(p)
-    need = smla.smla_fwd_workspace_size(p)
+    if w.page_size:
+        bt = x["block_table"].to(dev)
+        paged = smla.make_paged(bt, w.page_size)
+        need = smla.smla_fwd_paged_workspace_size(p, paged)
+    else:
+        need = smla.smla_fwd_workspace_size(p)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     p.workspace, p.workspace_bytes = ws.data_ptr(), ws.numel()
     stream = torch.cuda.current_stream()
 
     def step():
-        smla.smla_fwd(p, stream.cuda_stream)
+        if w.page_size:
+            smla.smla_fwd_paged(p, paged, stream.cuda_stream)
+        else:
+            smla.smla_fwd(p, stream.cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -191,6 +222,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "s_q": w.s_q, "h_q": w.h_q, "topk": w.topk, "s_kv": w.s_kv,
                    "d_qk": 576, "d_v": 512, "kv_format": fmt, "num_splits": plan_splits,
+                   "page_size": w.page_size or None,
                    "b_topk": plan_bt, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),

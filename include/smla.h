@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 1
+#define SMLA_ABI_VERSION 2
 
 /* The MLA shapes the kernels are built for: the query/key width d_qk is the
  * 512-wide latent plus the 64-wide rotary part, and V is the first 512 KV
@@ -139,6 +139,45 @@ smla_status smla_fwd_workspace_size(const smla_fwd_params* p, size_t* bytes);
 
 /* Enqueue the forward pass: writes out and lse.  Asynchronous on `stream`. */
 smla_status smla_fwd(const smla_fwd_params* p, void* stream);
+
+/* ---- Paged KV cache.
+ *
+ * Page "Flash Attention Infer算子性能优化" (catlass), section
+ * 优化Paged Attention路径: the KV cache lives in fixed-size pages whose rows are
+ * contiguous, and a block table names, in order, the physical page holding
+ * each logical block of a sequence.  Here every query token has its own block
+ * table row, and its indices name LOGICAL positions:
+ *
+ *   logical position j of token t  ->  physical KV row
+ *       block_table[t][j / page_size] * page_size + j % page_size
+ *
+ * of the KV tensor described by smla_fwd_params (kv, kv_stride_row,
+ * kv_format), whose s_kv is the physical row count num_pages * page_size.
+ * A slot is masked (weight zero, row never read) when its position is outside
+ * [0, table_width * page_size) or its block's table entry is outside
+ * [0, num_pages) (for example -1 for an unallocated block).  Everything else
+ * is smla_fwd: same outputs, plans, splits and formats. */
+typedef struct smla_paged_kv {
+  const int32_t* block_table;       /* DEVICE int32 [s_q, table_width], caller-owned */
+  int64_t block_table_stride_token; /* elements between consecutive tokens' rows, >= 0 */
+  int32_t table_width;              /* logical blocks per token, >= 1 */
+  int32_t page_size;                /* KV rows per page, >= 1; s_kv % page_size == 0 */
+} smla_paged_kv;
+
+/* Bytes of device workspace smla_fwd_paged needs: the translated indices
+ * (s_q * topk int32, rounded up to 256 bytes) followed by the split partials
+ * smla_fwd_workspace_size reports for the same parameters.  Never 0 when
+ * s_q > 0. */
+smla_status smla_fwd_paged_workspace_size(const smla_fwd_params* p, const smla_paged_kv* paged,
+                                          size_t* bytes);
+
+/* Enqueue the forward pass over a paged KV cache: one pass translates every
+ * token's logical indices to physical rows (into the workspace), then the
+ * forward pass of smla_fwd runs on them.  p->indices holds logical positions;
+ * p->workspace must hold smla_fwd_paged_workspace_size bytes (256-byte
+ * aligned).  Validation and error behaviour as smla_fwd, plus the block table
+ * (non-NULL when s_q > 0, 4-byte aligned) and the page geometry. */
+smla_status smla_fwd_paged(const smla_fwd_params* p, const smla_paged_kv* paged, void* stream);
 
 /* Host helper: pack E4M3 codes [rows, 576] and float32 scales [rows, 5]
  * (host memory, row-major, contiguous) into 640-byte fp8 KV rows at `packed`

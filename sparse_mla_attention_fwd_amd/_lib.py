@@ -30,8 +30,10 @@ MAX_SLOTS_PER_SPLIT = 2048
 MAX_SLOTS_PER_SPLIT_FP8 = 1536
 
 # Every symbol include/smla.h declares.
-EXPORTS = ("smla_fwd_plan", "smla_fwd_workspace_size", "smla_fwd", "smla_pack_fp8_kv_host",
-           "smla_status_string", "smla_last_error", "smla_abi_version")
+EXPORTS = ("smla_fwd_plan", "smla_fwd_workspace_size", "smla_fwd", "smla_fwd_paged_workspace_size",
+           "smla_fwd_paged", "smla_pack_fp8_kv_host", "smla_status_string", "smla_last_error",
+           "smla_abi_version")
+ABI_VERSION = 2
 
 
 class smla_fwd_params(ctypes.Structure):
@@ -47,6 +49,13 @@ class smla_fwd_params(ctypes.Structure):
         ("lse", ctypes.c_void_p), ("lse_stride_token", ctypes.c_int64),
         ("num_splits", ctypes.c_int32), ("b_topk", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class smla_paged_kv(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p), ("block_table_stride_token", ctypes.c_int64),
+        ("table_width", ctypes.c_int32), ("page_size", ctypes.c_int32),
     ]
 
 
@@ -74,6 +83,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.smla_fwd_workspace_size.restype = ctypes.c_int
     lib.smla_fwd.argtypes = [P, ctypes.c_void_p]
     lib.smla_fwd.restype = ctypes.c_int
+    G = ctypes.POINTER(smla_paged_kv)
+    lib.smla_fwd_paged_workspace_size.argtypes = [P, G, ctypes.POINTER(ctypes.c_size_t)]
+    lib.smla_fwd_paged_workspace_size.restype = ctypes.c_int
+    lib.smla_fwd_paged.argtypes = [P, G, ctypes.c_void_p]
+    lib.smla_fwd_paged.restype = ctypes.c_int
     lib.smla_pack_fp8_kv_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.smla_pack_fp8_kv_host.restype = ctypes.c_int
     lib.smla_status_string.argtypes = [ctypes.c_int32]
@@ -82,8 +96,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.smla_last_error.restype = ctypes.c_char_p
     lib.smla_abi_version.argtypes = []
     lib.smla_abi_version.restype = ctypes.c_int32
-    if lib.smla_abi_version() != 1:
-        raise ImportError(f"libsmla ABI version {lib.smla_abi_version()} != 1")
+    if lib.smla_abi_version() != ABI_VERSION:
+        raise ImportError(f"libsmla ABI version {lib.smla_abi_version()} != {ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -117,6 +131,28 @@ def smla_fwd(params: smla_fwd_params, stream: int | None = None):
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
     _check(load().smla_fwd(ctypes.byref(params), ctypes.c_void_p(stream)))
+
+
+def smla_fwd_paged_workspace_size(params: smla_fwd_params, paged: smla_paged_kv) -> int:
+    n = ctypes.c_size_t()
+    _check(load().smla_fwd_paged_workspace_size(ctypes.byref(params), ctypes.byref(paged), ctypes.byref(n)))
+    return n.value
+
+
+def smla_fwd_paged(params: smla_fwd_params, paged: smla_paged_kv, stream: int | None = None):
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    _check(load().smla_fwd_paged(ctypes.byref(params), ctypes.byref(paged), ctypes.c_void_p(stream)))
+
+
+def make_paged(block_table: torch.Tensor, page_size: int) -> smla_paged_kv:
+    """smla_paged_kv for an int32 block table [s_q, table_width]."""
+    g = smla_paged_kv()
+    g.block_table = block_table.data_ptr()
+    g.block_table_stride_token = block_table.stride(0)
+    g.table_width = block_table.shape[1]
+    g.page_size = int(page_size)
+    return g
 
 
 def smla_pack_fp8_kv_host(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:

@@ -138,6 +138,80 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   return SMLA_OK;
 }
 
+// Fill the kernel arguments for a checked plan and launch it.  idx/idx_st:
+// the (physical) indices to use; split_ws: the split-partials region.
+smla_status launch_plan(const smla_fwd_params* p, const Plan& pl, const int32_t* idx, int64_t idx_st,
+                        char* split_ws, hipStream_t stream) {
+  smla::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(p->q);
+  a.q_st = p->q_stride_token;
+  a.q_sh = p->q_stride_head;
+  a.kv = static_cast<const char*>(p->kv);
+  a.kv_row_bytes = p->kv_format == SMLA_KV_BF16 ? p->kv_stride_row * 2 : p->kv_stride_row;
+  a.idx = idx;
+  a.idx_st = idx_st;
+  a.out = static_cast<uint16_t*>(p->out);
+  a.out_st = p->out_stride_token;
+  a.out_sh = p->out_stride_head;
+  a.lse = p->lse;
+  a.lse_st = p->lse_stride_token;
+  if (pl.num_splits > 1) {
+    const size_t parts = (size_t)p->s_q * pl.num_splits * p->h_q;
+    a.ws_lse = reinterpret_cast<float*>(split_ws);
+    a.ws_o = reinterpret_cast<uint16_t*>(split_ws + ((parts * sizeof(float) + 255) & ~size_t(255)));
+  }
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.topk = p->topk;
+  a.slots_per_split = pl.slots_per_split;
+  a.num_splits = pl.num_splits;
+  a.head_groups = p->h_q > 64 ? p->h_q / 64 : 1;
+  a.inner_groups = 1;
+  if (p->kv_format == SMLA_KV_BF16 && p->h_q > 64 && pl.slots_per_split <= kRingSlots) {
+    // Every block of a split fits in the gather ring at once: one workgroup
+    // gathers the rows once and runs all head groups over them.
+    a.inner_groups = a.head_groups;
+    a.head_groups = 1;
+  }
+  a.s_kv = p->s_kv;
+  a.scale_log2 = p->sm_scale * 1.4426950408889634f;
+  {
+    const int64_t row_len = p->kv_format == SMLA_KV_BF16 ? 2 * SMLA_D_QK : SMLA_FP8_ROW_BYTES;
+    const int64_t window = p->s_kv > 0 ? (p->s_kv - 1) * a.kv_row_bytes + row_len : 0;
+    a.kv_window_bytes = window > 0 && window <= (int64_t)smla::kDummyOffset ? (uint32_t)window : 0u;
+  }
+  const hipError_t e = smla::launch_fwd(a, pl.b_topk, p->kv_format == SMLA_KV_FP8_E4M3, stream);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+// Paged-KV arguments (the base parameters are already checked).
+smla_status check_paged(const smla_fwd_params* p, const smla_paged_kv* pg) {
+  if (!pg) return fail(SMLA_ERR_INVALID_ARGUMENT, "paged is NULL");
+  if (pg->page_size < 1) return fail(SMLA_ERR_INVALID_ARGUMENT, "page_size=%d must be >= 1", pg->page_size);
+  if (pg->table_width < 1)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "table_width=%d must be >= 1", pg->table_width);
+  if ((int64_t)pg->table_width * pg->page_size > 2147483647LL)
+    return fail(SMLA_ERR_UNSUPPORTED, "table_width*page_size exceeds the int32 logical positions");
+  if (p->s_kv % pg->page_size)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "s_kv=%lld is not a whole number of pages of %d rows",
+                (long long)p->s_kv, pg->page_size);
+  if (pg->block_table_stride_token < 0)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "block_table_stride_token=%lld is negative",
+                (long long)pg->block_table_stride_token);
+  if (p->s_q > 0) {
+    if (!pg->block_table) return fail(SMLA_ERR_INVALID_ARGUMENT, "block_table is NULL");
+    if (reinterpret_cast<uintptr_t>(pg->block_table) % 4)
+      return fail(SMLA_ERR_INVALID_ARGUMENT, "block_table must be 4-byte aligned");
+  }
+  return SMLA_OK;
+}
+
+// Bytes of the translated-index region at the start of a paged workspace.
+size_t translated_bytes(const smla_fwd_params* p) {
+  return ((size_t)p->s_q * (size_t)p->topk * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
 }  // namespace
 
 extern "C" {
@@ -172,49 +246,43 @@ smla_status smla_fwd(const smla_fwd_params* p, void* stream) {
     if (reinterpret_cast<uintptr_t>(p->workspace) % 256)
       return fail(SMLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   }
-  smla::FwdArgs a{};
-  a.q = static_cast<const uint16_t*>(p->q);
-  a.q_st = p->q_stride_token;
-  a.q_sh = p->q_stride_head;
-  a.kv = static_cast<const char*>(p->kv);
-  a.kv_row_bytes = p->kv_format == SMLA_KV_BF16 ? p->kv_stride_row * 2 : p->kv_stride_row;
-  a.idx = p->indices;
-  a.idx_st = p->indices_stride_token;
-  a.out = static_cast<uint16_t*>(p->out);
-  a.out_st = p->out_stride_token;
-  a.out_sh = p->out_stride_head;
-  a.lse = p->lse;
-  a.lse_st = p->lse_stride_token;
-  if (pl.num_splits > 1) {
-    const size_t parts = (size_t)p->s_q * pl.num_splits * p->h_q;
-    a.ws_lse = static_cast<float*>(p->workspace);
-    a.ws_o = reinterpret_cast<uint16_t*>(static_cast<char*>(p->workspace) +
-                                         ((parts * sizeof(float) + 255) & ~size_t(255)));
-  }
-  a.s_q = p->s_q;
-  a.h_q = p->h_q;
-  a.topk = p->topk;
-  a.slots_per_split = pl.slots_per_split;
-  a.num_splits = pl.num_splits;
-  a.head_groups = p->h_q > 64 ? p->h_q / 64 : 1;
-  a.inner_groups = 1;
-  if (p->kv_format == SMLA_KV_BF16 && p->h_q > 64 && pl.slots_per_split <= kRingSlots) {
-    // Every block of a split fits in the gather ring at once: one workgroup
-    // gathers the rows once and runs all head groups over them.
-    a.inner_groups = a.head_groups;
-    a.head_groups = 1;
-  }
-  a.s_kv = p->s_kv;
-  a.scale_log2 = p->sm_scale * 1.4426950408889634f;
-  {
-    const int64_t row_len = p->kv_format == SMLA_KV_BF16 ? 2 * SMLA_D_QK : SMLA_FP8_ROW_BYTES;
-    const int64_t window = p->s_kv > 0 ? (p->s_kv - 1) * a.kv_row_bytes + row_len : 0;
-    a.kv_window_bytes = window > 0 && window <= (int64_t)smla::kDummyOffset ? (uint32_t)window : 0u;
-  }
-  const hipError_t e = smla::launch_fwd(a, pl.b_topk, p->kv_format == SMLA_KV_FP8_E4M3,
-                                        static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return launch_plan(p, pl, p->indices, p->indices_stride_token, static_cast<char*>(p->workspace),
+                     static_cast<hipStream_t>(stream));
+}
+
+smla_status smla_fwd_paged_workspace_size(const smla_fwd_params* p, const smla_paged_kv* pg,
+                                          size_t* bytes) {
+  if (!bytes) return fail(SMLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan pl;
+  smla_status s = check_and_plan(p, &pl);
+  if (s != SMLA_OK) return s;
+  s = check_paged(p, pg);
+  if (s != SMLA_OK) return s;
+  *bytes = translated_bytes(p) + pl.workspace_bytes;
   return SMLA_OK;
+}
+
+smla_status smla_fwd_paged(const smla_fwd_params* p, const smla_paged_kv* pg, void* stream) {
+  Plan pl;
+  smla_status s = check_and_plan(p, &pl);
+  if (s != SMLA_OK) return s;
+  s = check_paged(p, pg);
+  if (s != SMLA_OK) return s;
+  if (p->s_q == 0) return SMLA_OK;
+  const size_t tb = translated_bytes(p);
+  const size_t need = tb + pl.workspace_bytes;
+  if (!p->workspace || p->workspace_bytes < need)
+    return fail(SMLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                p->workspace ? p->workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(p->workspace) % 256)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  int32_t* phys = static_cast<int32_t*>(p->workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = smla::launch_paged_translate(
+      p->indices, p->indices_stride_token, pg->block_table, pg->block_table_stride_token,
+      pg->table_width, pg->page_size, p->s_kv / pg->page_size, p->s_q, p->topk, phys, st);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return launch_plan(p, pl, phys, p->topk, static_cast<char*>(p->workspace) + tb, st);
 }
 
 smla_status smla_pack_fp8_kv_host(const uint8_t* codes, const float* scales, int64_t rows,

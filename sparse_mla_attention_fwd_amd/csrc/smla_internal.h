@@ -56,6 +56,13 @@ struct FwdArgs {
 // launches.
 hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream);
 
+// Paged KV: logical index -> physical row through each token's block table
+// (-1 when masked), written contiguously to phys [s_q, topk].
+hipError_t launch_paged_translate(const int32_t* idx, int64_t idx_st, const int32_t* block_table,
+                                  int64_t bt_st, int32_t table_width, int32_t page_size,
+                                  int64_t num_pages, int32_t s_q, int32_t topk, int32_t* phys,
+                                  hipStream_t stream);
+
 // Forward kernel launchers per configuration (NW = waves per workgroup =
 // heads per workgroup / 16; BT = B_TOPK), each instantiated in its own
 // translation unit.

@@ -56,7 +56,41 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
   if (q8 == 0) a.lse[token * a.lse_st + head] = z > 0.f ? m + __logf(z) : kNegInf;
 }
 
+// Paged KV cache (page "Flash Attention Infer算子性能优化", section
+// 优化Paged Attention路径: pages of contiguous rows reached through a block
+// table).  One thread per slot: logical position v of token t is row
+// v % page_size of physical page block_table[t][v / page_size]; positions
+// outside [0, table_width * page_size) and blocks whose entry is outside
+// [0, num_pages) give -1 (masked by the forward kernels).
+__global__ __launch_bounds__(256) void smla_paged_translate_kernel(
+    const int32_t* __restrict__ idx, int64_t idx_st, const int32_t* __restrict__ bt, int64_t bt_st,
+    int32_t table_width, int32_t page_size, int64_t num_pages, int32_t s_q, int32_t topk,
+    int32_t* __restrict__ phys) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)s_q * topk) return;
+  const int64_t t = i / topk, j = i - t * topk;
+  const int32_t v = idx[t * idx_st + j];
+  int32_t r = -1;
+  if (v >= 0 && (int64_t)v < (int64_t)table_width * page_size) {
+    const int32_t blk = v / page_size;
+    const int32_t page = bt[t * bt_st + blk];
+    if (page >= 0 && (int64_t)page < num_pages) r = page * page_size + (v - blk * page_size);
+  }
+  phys[i] = r;
+}
+
 }  // namespace
+
+hipError_t launch_paged_translate(const int32_t* idx, int64_t idx_st, const int32_t* block_table,
+                                  int64_t bt_st, int32_t table_width, int32_t page_size,
+                                  int64_t num_pages, int32_t s_q, int32_t topk, int32_t* phys,
+                                  hipStream_t stream) {
+  const int64_t n = (int64_t)s_q * topk;
+  hipLaunchKernelGGL(smla_paged_translate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, idx, idx_st, block_table, bt_st, table_width, page_size, num_pages, s_q,
+                     topk, phys);
+  return hipGetLastError();
+}
 
 hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream) {
   hipError_t e;

@@ -28,28 +28,29 @@ def test_library_exports_every_declared_function():
     assert sorted(declared) == sorted(_lib.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.smla_abi_version() == 1
+    assert lib.smla_abi_version() == _lib.ABI_VERSION
 
 
-def test_params_struct_layout_matches_header(tmp_path):
-    """Every field offset of the ctypes mirror equals the C compiler's."""
+@pytest.mark.parametrize("struct,cname", [(_lib.smla_fwd_params, "smla_fwd_params"),
+                                          (_lib.smla_paged_kv, "smla_paged_kv")])
+def test_struct_layouts_match_header(tmp_path, struct, cname):
+    """Every field offset of the ctypes mirrors equals the C compiler's."""
     import shutil
     import subprocess
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no C compiler to read the header's layout")
-    fields = [f for f, _ in _lib.smla_fwd_params._fields_]
+    fields = [f for f, _ in struct._fields_]
     src = tmp_path / "off.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "smla.h"\nint main(void){\n'
-                   + f'printf("%zu\\n", sizeof(smla_fwd_params));\n'
-                   + "".join(f'printf("%zu\\n", offsetof(smla_fwd_params, {f}));\n' for f in fields)
+                   + f'printf("%zu\\n", sizeof({cname}));\n'
+                   + "".join(f'printf("%zu\\n", offsetof({cname}, {f}));\n' for f in fields)
                    + "return 0;}\n")
     exe = tmp_path / "off"
     subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    P = _lib.smla_fwd_params
-    assert got[0] == ctypes.sizeof(P)
-    assert got[1:] == [getattr(P, f).offset for f in fields]
+    assert got[0] == ctypes.sizeof(struct)
+    assert got[1:] == [getattr(struct, f).offset for f in fields]
 
 
 FAKE = 1 << 20   # 16-byte aligned fake device addresses: never dereferenced on failure paths
@@ -177,3 +178,45 @@ def test_pack_fp8_rows_host():
     assert torch.equal(packed[:, :576], codes)
     assert torch.equal(packed[:, 576:596].contiguous().view(torch.float32), scales)
     assert torch.all(packed[:, 596:] == 0)
+
+
+def _paged(**kw):
+    g = _lib.smla_paged_kv()
+    g.block_table, g.block_table_stride_token, g.table_width, g.page_size = FAKE * 7, 32, 32, 64
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("page_size", 0, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("page_size", 3, _lib.SMLA_ERR_INVALID_ARGUMENT),        # s_kv 2048 is not whole pages of 3
+    ("table_width", 0, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("table_width", 1 << 30, _lib.SMLA_ERR_UNSUPPORTED),     # logical positions past int32
+    ("block_table", 0, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("block_table", FAKE + 2, _lib.SMLA_ERR_INVALID_ARGUMENT),
+    ("block_table_stride_token", -1, _lib.SMLA_ERR_INVALID_ARGUMENT),
+])
+def test_paged_arguments_are_rejected_on_the_host(field, value, status):
+    lib = _lib.load()
+    p = _params()
+    g = _paged(**{field: value})
+    assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == status
+    assert _lib.last_error() != ""
+    n = ctypes.c_size_t(123)
+    assert lib.smla_fwd_paged_workspace_size(ctypes.byref(p), ctypes.byref(g), ctypes.byref(n)) == status
+
+
+def test_paged_workspace_and_null_paged():
+    lib = _lib.load()
+    p = _params()
+    assert lib.smla_fwd_paged(ctypes.byref(p), None, None) == _lib.SMLA_ERR_INVALID_ARGUMENT
+    g = _paged()
+    # translated indices first (s_q * topk int32, 256-byte rounded), then the split region
+    p.num_splits = 1
+    assert _lib.smla_fwd_paged_workspace_size(p, g) == 4 * 128 * 4
+    p.num_splits = 3
+    assert _lib.smla_fwd_paged_workspace_size(p, g) == 4 * 128 * 4 + _lib.smla_fwd_workspace_size(p)
+    assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == _lib.SMLA_ERR_WORKSPACE
+    p.s_q = 0
+    assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == _lib.SMLA_OK

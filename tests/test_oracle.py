@@ -15,6 +15,7 @@ import torch
 from oracle import (RESCALE_THRES, dequant_fp8_rows, e4m3fn_decode, lse_combine,
                     sparse_mla_fwd_exact, sparse_mla_fwd_online, sparse_mla_fwd_split)
 from oracle.cost_model import cost_model_cycles
+from oracle.paged import sparse_mla_fwd_paged
 from oracle.sparse_mla import round_to_bf16, split_bounds
 import workloads
 
@@ -305,3 +306,84 @@ def test_online_bf16_numerics_model_is_within_tolerance():
     err = np.abs(o - o2).max() / np.abs(o).max()
     assert 0 < err < 2e-3
     assert np.allclose(l, l2, atol=1e-12)
+
+
+# ---- paged KV cache (page "Flash Attention Infer算子性能优化", section
+# 优化Paged Attention路径): logical position j of token t is row j % page_size
+# of page block_table[t, j // page_size].
+
+def _paged_case(seed, s_q=4, h_q=3, d_qk=10, d_v=6, page_size=3, num_pages=7, width=4, topk=9):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((s_q, h_q, d_qk))
+    pages = rng.standard_normal((num_pages, page_size, d_qk))
+    # pages shared between tokens, unallocated blocks (-1, num_pages + 2)
+    table = rng.integers(0, num_pages, (s_q, width))
+    table[0, 1] = -1
+    if s_q > 2:
+        table[2, 3] = num_pages + 2
+    idx = rng.integers(-2, width * page_size + 2, (s_q, topk))
+    return q, pages, table, idx, 0.41, d_v
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_paged_matches_brute_force_on_translated_rows(seed):
+    """Brute force along another route: translate every logical index to a
+    physical row of the flattened page pool with scalar Python arithmetic,
+    then the plain loops of _brute over the pool."""
+    q, pages, table, idx, sc, d_v = _paged_case(seed)
+    num_pages, ps, d_qk = pages.shape
+    width = table.shape[1]
+    phys = np.full(idx.shape, -1, dtype=np.int64)
+    for t in range(idx.shape[0]):
+        for j in range(idx.shape[1]):
+            v = int(idx[t, j])
+            if 0 <= v < width * ps:
+                page = int(table[t, v // ps])
+                if 0 <= page < num_pages:
+                    phys[t, j] = page * ps + v % ps
+    ob, lb = _brute(q, pages.reshape(-1, d_qk), phys, sc, d_v)
+    o, l = sparse_mla_fwd_paged(q, pages, table, idx, sc, d_v)
+    assert np.allclose(o, ob, rtol=0, atol=1e-12)
+    assert np.array_equal(np.isinf(l), np.isinf(lb))
+    fin = np.isfinite(lb)
+    assert np.allclose(l[fin], lb[fin], rtol=0, atol=1e-12)
+
+
+def test_paged_identity_table_is_the_flat_cache():
+    q, kv, idx, sc, d_v = _rand_case(5, s_kv=12, invalid=0.3)
+    ps = 4
+    pages = kv.reshape(3, ps, kv.shape[1])
+    table = np.tile(np.arange(3), (q.shape[0], 1))
+    o, l = sparse_mla_fwd_paged(q, pages, table, idx, sc, d_v)
+    oe, le = sparse_mla_fwd_exact(q, kv, idx, sc, d_v)
+    assert np.array_equal(o, oe) and np.array_equal(l, le)
+
+
+def test_paged_result_ignores_where_pages_live():
+    """Moving the physical pages and rewriting the table accordingly leaves
+    every output unchanged."""
+    q, pages, table, idx, sc, d_v = _paged_case(9)
+    perm = np.random.default_rng(1).permutation(pages.shape[0])
+    moved = np.empty_like(pages)
+    moved[perm] = pages                              # page p now lives at perm[p]
+    ok = (table >= 0) & (table < pages.shape[0])
+    table2 = np.where(ok, perm[np.clip(table, 0, pages.shape[0] - 1)], table)
+    a = sparse_mla_fwd_paged(q, pages, table, idx, sc, d_v)
+    b = sparse_mla_fwd_paged(q, moved, table2, idx, sc, d_v)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_paged_unallocated_block_and_one_row():
+    """All valid slots name logical row r: out = V[r] exactly and
+    lse = x_r + ln(count); slots into an unallocated block or past the table
+    change nothing."""
+    q, pages, table, idx, sc, d_v = _paged_case(4, s_q=1)
+    ps = pages.shape[1]
+    table[0] = [2, -1, 5, 0]
+    r = 2 * ps + 1                                   # logical row in page 5
+    idx[0] = [r, r, ps, ps + 2, r, 4 * ps, -1, r, r]  # ps.. in the unallocated block
+    o, l = sparse_mla_fwd_paged(q, pages, table, idx, sc, d_v)
+    v = pages[5, 1]
+    assert np.allclose(o[0], np.broadcast_to(v[:d_v], o[0].shape), rtol=0, atol=1e-13)
+    x = float(np.float32(sc)) * (q[0] @ v)
+    assert np.allclose(l[0], x + math.log(5), rtol=0, atol=1e-12)

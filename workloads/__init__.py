@@ -18,6 +18,10 @@ to nearest even, torch's cast).  The five named workloads:
 * ``decode``:     64 sequences x 1 token, h_q 128, topk 512, 32768 KV rows per
                   sequence stacked into one [64*32768, 576] tensor; indices are
                   global row ids inside the token's own sequence; 4 splits.
+* ``decode_paged``: the ``decode`` shapes over a paged KV cache: pages of 64
+                  rows, the 32768 pages of the pool dealt to the 64 sequences in
+                  a random order (each sequence's block table lists its 512
+                  pages); indices are logical positions in [0, 32768).
 * ``decode_fp8``: 128 sequences x 1 token, h_q 64, topk 2048, 16384 rows per
                   sequence, KV quantised to FP8 E4M3 with one float32 scale per
                   128-column group of each row (scale = absmax / 448, code =
@@ -54,6 +58,7 @@ class Workload:
     q_mult: float = 1.0
     kv_format: str = "bf16"  # "bf16" or "fp8"
     num_splits: int = 1      # split-topk parts the workload asks for (0: auto)
+    page_size: int = 0       # paged KV: rows per page (0: not paged)
     seed: int = 0
 
     @property
@@ -79,6 +84,8 @@ WORKLOADS = {
                        q_mult=4.0, seed=3),
     "decode": Workload("decode", s_q=64, h_q=128, topk=512, s_kv=64 * 32768, seqs=64,
                        rows_per_seq=32768, num_splits=4, seed=4),
+    "decode_paged": Workload("decode_paged", s_q=64, h_q=128, topk=512, s_kv=64 * 32768, seqs=64,
+                             rows_per_seq=32768, num_splits=4, page_size=64, seed=6),
     "decode_fp8": Workload("decode_fp8", s_q=128, h_q=64, topk=2048, s_kv=128 * 16384,
                            seqs=128, rows_per_seq=16384, kv_format="fp8", num_splits=0,
                            seed=5),
@@ -128,6 +135,9 @@ def _indices(rng: np.random.Generator, w: Workload) -> np.ndarray:
                 idx[t, :n] = rng.permutation(n)
             else:
                 idx[t] = rng.choice(n, w.topk, replace=False)
+    elif w.page_size:
+        for b in range(w.s_q):               # logical positions in the sequence
+            idx[b] = rng.choice(w.rows_per_seq, w.topk, replace=False)
     elif w.seqs > 1:
         for b in range(w.s_q):
             idx[b] = b * w.rows_per_seq + rng.choice(w.rows_per_seq, w.topk, replace=False)
@@ -143,7 +153,9 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> dict:
     Returns a dict with ``q`` (bf16 [s_q, h_q, 576]), ``indices`` (int32
     [s_q, topk]), ``sm_scale`` (float), ``d_v`` (512), and either ``kv`` (bf16
     [s_kv, 576]) or ``kv_codes`` (uint8 [s_kv, 576]) with ``kv_scales``
-    (float32 [s_kv, 5]) for the fp8 workload.
+    (float32 [s_kv, 5]) for the fp8 workload.  Paged workloads add
+    ``block_table`` (int32 [s_q, pages per sequence]) and ``page_size``; their
+    ``kv`` is the page pool, rows of page p at [p * page_size, (p+1) * page_size).
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -157,6 +169,12 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> dict:
     else:
         out["kv"] = _normal_bf16(rng, (w.s_kv, D_QK))
     out["indices"] = torch.from_numpy(_indices(rng, w))
+    if w.page_size:
+        # the pool's pages dealt to the sequences in a random order
+        per = w.rows_per_seq // w.page_size
+        perm = rng.permutation(w.s_kv // w.page_size).astype(np.int32)
+        out["block_table"] = torch.from_numpy(perm[: w.s_q * per].reshape(w.s_q, per).copy())
+        out["page_size"] = w.page_size
     return out
 
 
@@ -201,3 +219,28 @@ def make_random(*, s_q: int, h_q: int, topk: int, s_kv: int, seed: int,
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a bf16/float32 tensor (for the oracle)."""
     return t.to(torch.float64).numpy()
+
+
+def make_random_paged(*, s_q: int, h_q: int, topk: int, page_size: int, num_pages: int,
+                      table_width: int, seed: int, unallocated_frac: float = 0.0,
+                      invalid_frac: float = 0.0, kv_format: str = "bf16") -> dict:
+    """Small seeded paged cases: a pool of ``num_pages`` pages of ``page_size``
+    rows (``kv`` or ``kv_codes``/``kv_scales`` of num_pages * page_size rows),
+    a block table of random pages (repeats across and within tokens allowed),
+    ``unallocated_frac`` of its entries -1, and logical indices uniform over
+    [0, table_width * page_size) with ``invalid_frac`` of them out of range."""
+    rng = np.random.default_rng(seed)
+    res = make_random(s_q=s_q, h_q=h_q, topk=1, s_kv=num_pages * page_size, seed=seed,
+                      kv_format=kv_format)
+    table = rng.integers(0, num_pages, (s_q, table_width)).astype(np.int32)
+    if unallocated_frac > 0:
+        table[rng.random((s_q, table_width)) < unallocated_frac] = -1
+    n = table_width * page_size
+    idx = rng.integers(0, n, (s_q, topk)).astype(np.int64)
+    if invalid_frac > 0:
+        m = rng.random((s_q, topk)) < invalid_frac
+        idx = np.where(m, rng.choice(np.array([-1, n, n + 5, -(2 ** 31)], dtype=np.int64), (s_q, topk)), idx)
+    res["indices"] = torch.from_numpy(idx.astype(np.int32))
+    res["block_table"] = torch.from_numpy(table)
+    res["page_size"] = page_size
+    return res
