@@ -14,7 +14,9 @@ replacement per token.
 
 ``roofline``: algorithmic FLOPs of one launch (2·h_q·(d_qk + d_v) per valid
 slot) over the average launch duration, measured with HIP events recorded on
-the stream the kernel runs on, against the MI355X dense bf16 MFMA peak.
+the stream the kernel runs on, against the MI355X dense bf16 MFMA peak; for
+the decode workloads (HBM-bound) the algorithmic bytes of one launch over the
+same duration against the 8 TB/s HBM peak.
 ``cpu_baseline``: the float64 CPU oracle timed on this host over a bounded
 sample of the same workload's tokens.
 """
@@ -57,6 +59,17 @@ def load_traffic(workload: str, per_launch_flops: float):
     if rec.get("kernel_hash") != kernel_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(w) -> int:
+    """HBM bytes one launch must move at least: every valid slot's KV row
+    (1152 bytes bf16; 576 code bytes + 20 scale bytes fp8) when the rows are
+    not reused (decode: each sequence's slots are distinct rows of its own
+    cache), else the KV once; plus Q, out, lse, the indices and a block table."""
+    row = 1152 if w.kv_format == "bf16" else 596
+    kv = w.valid_slots * row if w.seqs > 1 else w.s_kv * row
+    table = w.s_q * (w.rows_per_seq // w.page_size) * 4 if w.page_size else 0
+    return kv + w.s_q * w.h_q * (576 + 512) * 2 + w.s_q * w.h_q * 4 + w.s_q * w.topk * 4 + table
 
 
 def cpu_baseline(x, budget_s: float):
@@ -207,6 +220,17 @@ def main():
     row_bytes = 1152 if fmt == "bf16" else 640
     gathered = w.valid_slots * row_bytes
 
+    if w.seqs > 1:
+        # decode: HBM-bound (arithmetic intensity below the MFMA/HBM ridge)
+        alg = algorithmic_bytes(w)
+        gbs = alg / avg_launch_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes": alg, "tflops": round(achieved, 2)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": traffic}
     res = {
         "metric": "sparse MLA fwd TFLOP/s and % bf16 MFMA peak (h_q=64, topk=2048, d_qk=576)",
         "value": round(value, 2),
@@ -224,9 +248,7 @@ def main():
                    "d_qk": 576, "d_v": 512, "kv_format": fmt, "num_splits": plan_splits,
                    "page_size": w.page_size or None,
                    "b_topk": plan_bt, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic},
+        "roofline": roofline,
         "gather": {"bytes_per_launch": gathered, "GB/s": round(gathered / avg_launch_s / 1e9, 1),
                    "frac_of_hbm_peak": round(gathered / avg_launch_s / 1e9 / HBM_PEAK_GBS, 4)},
         "avg_launch_ms": round(avg_launch_s * 1e3, 4),
