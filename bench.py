@@ -63,10 +63,10 @@ def load_traffic(workload: str, per_launch_flops: float):
 
 def algorithmic_bytes(w) -> int:
     """HBM bytes one launch must move at least: every valid slot's KV row
-    (1152 bytes bf16; 576 code bytes + 20 scale bytes fp8) when the rows are
+    (1152 bytes bf16; 576 (fp8) or 288 (fp4) code bytes + 20 scale bytes) when the rows are
     not reused (decode: each sequence's slots are distinct rows of its own
     cache), else the KV once; plus Q, out, lse, the indices and a block table."""
-    row = 1152 if w.kv_format == "bf16" else 596
+    row = {"bf16": 1152, "fp8": 576 + 20, "fp4": 288 + 20}[w.kv_format]
     kv = w.valid_slots * row if w.seqs > 1 else w.s_kv * row
     table = w.s_q * (w.rows_per_seq // w.page_size) * 4 if w.page_size else 0
     return kv + w.s_q * w.h_q * (576 + 512) * 2 + w.s_q * w.h_q * 4 + w.s_q * w.topk * 4 + table
@@ -102,17 +102,42 @@ def cpu_baseline(x, budget_s: float):
             done = sl.stop
         valid = int((idx[:done] >= 0).sum())
         return _cpu_result(w, valid, t_used, done, "paged float64 numpy")
-    kv = workloads.to_f64(x["kv"])
-    sparse_mla_fwd_exact(workloads.to_f64(x["q"][:1]), kv, idx[:1], x["sm_scale"], 512)  # warm BLAS
+    from oracle import dequant_fp4_rows, dequant_fp8_rows
+
+    def rows_f64(sel):
+        """float64 values of KV rows sel (exact for every format)."""
+        if w.kv_format == "bf16":
+            return workloads.to_f64(x["kv"][sel])
+        dq = dequant_fp8_rows if w.kv_format == "fp8" else dequant_fp4_rows
+        return dq(x["kv_codes"][sel].numpy(), x["kv_scales"][sel].numpy())
+
+    if w.seqs > 1:
+        # decode: each chunk's referenced rows only (the caches are GBs);
+        # float64 copies made outside the timing
+        def chunk_inputs(sl):
+            ii = idx[sl]
+            ok = (ii >= 0) & (ii < w.s_kv)
+            rows = np.unique(ii[ok])
+            remap = np.full(ii.shape, -1, dtype=np.int64)
+            remap[ok] = np.searchsorted(rows, ii[ok])
+            return rows_f64(torch.from_numpy(rows)), remap
+    else:
+        kv_all = rows_f64(torch.arange(w.s_kv))
+
+        def chunk_inputs(sl):
+            return kv_all, idx[sl]
+    kv0, i0 = chunk_inputs(slice(0, 1))
+    sparse_mla_fwd_exact(workloads.to_f64(x["q"][:1]), kv0, i0, x["sm_scale"], 512)  # warm BLAS
     while done < w.s_q and (t_used < budget_s or done < 16):
         sl = slice(done, min(w.s_q, done + chunk))
         q = workloads.to_f64(x["q"][sl])
+        kv, ii = chunk_inputs(sl)
         t0 = time.perf_counter()
-        sparse_mla_fwd_exact(q, kv, idx[sl], x["sm_scale"], 512)
+        sparse_mla_fwd_exact(q, kv, ii, x["sm_scale"], 512)
         t_used += time.perf_counter() - t0
         done = sl.stop
-    valid = ((idx[:done] >= 0) & (idx[:done] < kv.shape[0])).sum()
-    return _cpu_result(w, valid, t_used, done, "float64 numpy")
+    valid = ((idx[:done] >= 0) & (idx[:done] < w.s_kv)).sum()
+    return _cpu_result(w, valid, t_used, done, f"float64 numpy ({w.kv_format} KV values)")
 
 
 def _cpu_result(w, valid, t_used, done, kind):
@@ -167,15 +192,17 @@ def main():
     idx = x["indices"].to(dev)
     if w.kv_format == "fp8":
         kv = smla.pack_fp8_kv(x["kv_codes"], x["kv_scales"], dev)
-        fmt = "fp8"
+    elif w.kv_format == "fp4":
+        kv = smla.pack_fp4_kv(x["kv_codes"], x["kv_scales"], dev)
     else:
         kv = x["kv"].to(dev)
-        fmt = "bf16"
+    fmt = w.kv_format
     ns = w.num_splits if args.num_splits < 0 else args.num_splits
     out = torch.empty((w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.s_q, w.h_q), dtype=torch.float32, device=dev)
     p = smla.make_params(q, kv, idx, x["sm_scale"], out, lse,
-                         kv_format=smla.SMLA_KV_FP8_E4M3 if fmt == "fp8" else smla.SMLA_KV_BF16,
+                         kv_format={"bf16": smla.SMLA_KV_BF16, "fp8": smla.SMLA_KV_FP8_E4M3,
+                                    "fp4": smla.SMLA_KV_FP4_E2M1}[fmt],
                          num_splits=ns, b_topk=args.b_topk)
     plan_splits, plan_bt = smla.smla_fwd_plan(p)
     if w.page_size:
@@ -217,7 +244,7 @@ def main():
     value = flops / (ms_per_step / 1e3) / 1e12
     achieved = flops / avg_launch_s / 1e12
     traffic = load_traffic(w.name, flops)
-    row_bytes = 1152 if fmt == "bf16" else 640
+    row_bytes = {"bf16": 1152, "fp8": 640, "fp4": 320}[fmt]
     gathered = w.valid_slots * row_bytes
 
     if w.seqs > 1:

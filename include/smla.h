@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 2
+#define SMLA_ABI_VERSION 3
 
 /* The MLA shapes the kernels are built for: the query/key width d_qk is the
  * 512-wide latent plus the 64-wide rotary part, and V is the first 512 KV
@@ -64,8 +64,17 @@ extern "C" {
 #define SMLA_FP8_NUM_GROUPS 5
 #define SMLA_FP8_ROW_BYTES 640
 
+/* fp4 KV cache (the pages name an FP4 cache for decode beside the FP8 one,
+ * section on decoding): OCP MX E2M1 codes (1 sign, 2 exponent, 1 mantissa
+ * bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two per byte,
+ * with the same five float32 group scales.  A 320-byte row: bytes [0, 288)
+ * hold column 2k in the low nibble and column 2k+1 in the high nibble of byte
+ * k, bytes [288, 308) the five scales, bytes [308, 320) padding.
+ * Element value = e2m1(code) * scale[column / 128]. */
+#define SMLA_FP4_ROW_BYTES 320
+
 /* Largest number of slots one workgroup handles; the planner splits the topk
- * range of a token into parts no larger than this (bf16 KV / fp8 KV). */
+ * range of a token into parts no larger than this (bf16 and fp4 KV / fp8 KV). */
 #define SMLA_MAX_SLOTS_PER_SPLIT 2048
 #define SMLA_MAX_SLOTS_PER_SPLIT_FP8 1536
 
@@ -78,8 +87,9 @@ typedef enum smla_status {
 } smla_status;
 
 typedef enum smla_kv_format {
-  SMLA_KV_BF16 = 0,    /* kv: bf16 [s_kv, 576], kv_stride_row in elements */
-  SMLA_KV_FP8_E4M3 = 1 /* kv: packed 640-byte rows, kv_stride_row in BYTES */
+  SMLA_KV_BF16 = 0,     /* kv: bf16 [s_kv, 576], kv_stride_row in elements */
+  SMLA_KV_FP8_E4M3 = 1, /* kv: packed 640-byte rows, kv_stride_row in BYTES */
+  SMLA_KV_FP4_E2M1 = 2  /* kv: packed 320-byte rows, kv_stride_row in BYTES */
 } smla_kv_format;
 
 typedef struct smla_fwd_params {
@@ -183,6 +193,14 @@ smla_status smla_fwd_paged(const smla_fwd_params* p, const smla_paged_kv* paged,
  * (host memory, row-major, contiguous) into 640-byte fp8 KV rows at `packed`
  * (host memory, rows * 640 bytes, caller-owned).  Padding bytes are zeroed. */
 smla_status smla_pack_fp8_kv_host(const uint8_t* codes, const float* scales, int64_t rows,
+                                  void* packed);
+
+/* Host helper: pack E2M1 codes [rows, 576] (one 4-bit code per byte, values
+ * 0..15) and float32 scales [rows, 5] (host memory, row-major, contiguous)
+ * into 320-byte fp4 KV rows at `packed` (host memory, rows * 320 bytes,
+ * caller-owned).  A code above 15 is an invalid argument (nothing written
+ * past the check).  Padding bytes are zeroed. */
+smla_status smla_pack_fp4_kv_host(const uint8_t* codes, const float* scales, int64_t rows,
                                   void* packed);
 
 /* Static text for a status code. */

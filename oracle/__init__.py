@@ -23,6 +23,8 @@ the page "Ascend Sparse Attention Forward 算法与优化技术简析":
 * ``sparse_mla_fwd_paged`` -- the same definition over a paged KV cache
   reached through a per-token block table (page "Flash Attention
   Infer算子性能优化", section 优化Paged Attention路径).
+* ``e2m1_decode`` / ``dequant_fp4_rows`` -- the fp4 KV-cache values, decoded
+  from the OCP Microscaling specification's E2M1 element format.
 * ``e4m3fn_decode`` / ``dequant_fp8_rows`` -- the fp8 KV-cache values,
   decoded from the OCP 8-bit floating point specification (E4M3, "fn"
   variant: no infinities, max 448).
@@ -36,4 +38,5 @@ from .sparse_mla import (  # noqa: F401
     valid_slot_mask,
 )
 from .fp8 import e4m3fn_decode, dequant_fp8_rows, FP8_GROUP  # noqa: F401
+from .fp4 import e2m1_decode, dequant_fp4_rows  # noqa: F401
 from .paged import sparse_mla_fwd_paged, logical_sequence  # noqa: F401

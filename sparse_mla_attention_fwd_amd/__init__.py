@@ -19,19 +19,28 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (D_QK, D_V, FP8_ROW_BYTES, SMLA_KV_BF16, SMLA_KV_FP8_E4M3, SmlaError,  # noqa: F401
-                   make_paged, make_params, smla_fwd, smla_fwd_paged,
+from ._lib import (D_QK, D_V, FP4_ROW_BYTES, FP8_ROW_BYTES, SMLA_KV_BF16, SMLA_KV_FP4_E2M1,  # noqa: F401
+                   SMLA_KV_FP8_E4M3, SmlaError, make_paged, make_params, smla_fwd, smla_fwd_paged,
                    smla_fwd_paged_workspace_size, smla_fwd_plan, smla_fwd_workspace_size,
-                   smla_pack_fp8_kv_host)
+                   smla_pack_fp4_kv_host, smla_pack_fp8_kv_host)
 
-__all__ = ["sparse_mla_fwd", "pack_fp8_kv", "smla_fwd", "smla_fwd_plan", "smla_fwd_workspace_size",
-           "smla_fwd_paged", "smla_fwd_paged_workspace_size", "smla_pack_fp8_kv_host", "SmlaError"]
+__all__ = ["sparse_mla_fwd", "pack_fp8_kv", "pack_fp4_kv", "smla_fwd", "smla_fwd_plan",
+           "smla_fwd_workspace_size", "smla_fwd_paged", "smla_fwd_paged_workspace_size",
+           "smla_pack_fp8_kv_host", "smla_pack_fp4_kv_host", "SmlaError"]
 
 
 def pack_fp8_kv(codes: torch.Tensor, scales: torch.Tensor, device=None) -> torch.Tensor:
     """fp8 KV cache in the library's row format (codes and scales of a token
     side by side, 640 bytes per row), optionally moved to ``device``."""
     packed = smla_pack_fp8_kv_host(codes.cpu(), scales.cpu())
+    return packed.to(device) if device is not None else packed
+
+
+def pack_fp4_kv(codes: torch.Tensor, scales: torch.Tensor, device=None) -> torch.Tensor:
+    """fp4 KV cache in the library's row format (two E2M1 codes per byte, the
+    five group scales beside them, 320 bytes per row), optionally moved to
+    ``device``."""
+    packed = smla_pack_fp4_kv_host(codes.cpu(), scales.cpu())
     return packed.to(device) if device is not None else packed
 
 
@@ -44,7 +53,8 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
     """Run the forward pass on the tensors' GPU and return ``(out, lse)``.
 
     q: bf16 [s_q, h_q, 576]; kv: bf16 [s_kv, 576] or, with ``kv_format="fp8"``,
-    uint8 [s_kv, 640] packed rows (see ``pack_fp8_kv``); indices: int32
+    uint8 [s_kv, 640] packed rows (see ``pack_fp8_kv``), or with
+    ``kv_format="fp4"`` uint8 [s_kv, 320] (see ``pack_fp4_kv``); indices: int32
     [s_q, topk].  ``num_splits``/``b_topk`` 0 let the library plan.  Outputs and
     the split workspace are allocated with torch unless given.
 
@@ -55,13 +65,13 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
     """
     if not q.is_cuda:
         raise ValueError("sparse_mla_fwd runs on the GPU only: q must be a device tensor")
-    fmt = {"bf16": SMLA_KV_BF16, "fp8": SMLA_KV_FP8_E4M3}[kv_format]
+    fmt = {"bf16": SMLA_KV_BF16, "fp8": SMLA_KV_FP8_E4M3, "fp4": SMLA_KV_FP4_E2M1}[kv_format]
     if q.dtype != torch.bfloat16:
         raise TypeError("q must be bfloat16")
     if fmt == SMLA_KV_BF16 and kv.dtype != torch.bfloat16:
         raise TypeError("bf16 KV must be a bfloat16 tensor")
-    if fmt == SMLA_KV_FP8_E4M3 and kv.dtype != torch.uint8:
-        raise TypeError("fp8 KV must be a uint8 tensor of packed 640-byte rows")
+    if fmt != SMLA_KV_BF16 and kv.dtype != torch.uint8:
+        raise TypeError("quantised KV must be a uint8 tensor of packed rows")
     if indices.dtype != torch.int32:
         raise TypeError("indices must be int32")
     if (block_table is None) != (page_size is None):

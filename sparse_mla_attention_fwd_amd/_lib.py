@@ -21,19 +21,21 @@ SMLA_ERR_WORKSPACE = 3
 SMLA_ERR_HIP = 4
 SMLA_KV_BF16 = 0
 SMLA_KV_FP8_E4M3 = 1
+SMLA_KV_FP4_E2M1 = 2
 D_QK = 576
 D_V = 512
 FP8_GROUP = 128
 FP8_NUM_GROUPS = 5
 FP8_ROW_BYTES = 640
+FP4_ROW_BYTES = 320
 MAX_SLOTS_PER_SPLIT = 2048
 MAX_SLOTS_PER_SPLIT_FP8 = 1536
 
 # Every symbol include/smla.h declares.
 EXPORTS = ("smla_fwd_plan", "smla_fwd_workspace_size", "smla_fwd", "smla_fwd_paged_workspace_size",
-           "smla_fwd_paged", "smla_pack_fp8_kv_host", "smla_status_string", "smla_last_error",
-           "smla_abi_version")
-ABI_VERSION = 2
+           "smla_fwd_paged", "smla_pack_fp8_kv_host", "smla_pack_fp4_kv_host", "smla_status_string",
+           "smla_last_error", "smla_abi_version")
+ABI_VERSION = 3
 
 
 class smla_fwd_params(ctypes.Structure):
@@ -90,6 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.smla_fwd_paged.restype = ctypes.c_int
     lib.smla_pack_fp8_kv_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.smla_pack_fp8_kv_host.restype = ctypes.c_int
+    lib.smla_pack_fp4_kv_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.smla_pack_fp4_kv_host.restype = ctypes.c_int
     lib.smla_status_string.argtypes = [ctypes.c_int32]
     lib.smla_status_string.restype = ctypes.c_char_p
     lib.smla_last_error.argtypes = []
@@ -168,6 +172,20 @@ def smla_pack_fp8_kv_host(codes: torch.Tensor, scales: torch.Tensor) -> torch.Te
     return packed
 
 
+def smla_pack_fp4_kv_host(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """Pack host uint8 E2M1 codes [rows, 576] (one 4-bit code per byte) and
+    float32 scales [rows, 5] into 320-byte fp4 KV rows (a host uint8 tensor
+    [rows, 320])."""
+    codes = codes.contiguous()
+    scales = scales.to(torch.float32).contiguous()
+    assert codes.dtype == torch.uint8 and codes.dim() == 2 and codes.shape[1] == D_QK
+    assert scales.shape == (codes.shape[0], FP8_NUM_GROUPS)
+    rows = codes.shape[0]
+    packed = torch.empty((rows, FP4_ROW_BYTES), dtype=torch.uint8)
+    _check(load().smla_pack_fp4_kv_host(codes.data_ptr(), scales.data_ptr(), rows, packed.data_ptr()))
+    return packed
+
+
 def make_params(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float,
                 out: torch.Tensor, lse: torch.Tensor, *, kv_format: int = SMLA_KV_BF16,
                 s_kv: int | None = None, num_splits: int = 0, b_topk: int = 0) -> smla_fwd_params:
@@ -181,7 +199,7 @@ def make_params(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_sca
     p.sm_scale = float(sm_scale)
     p.q, p.q_stride_token, p.q_stride_head = q.data_ptr(), q.stride(0), q.stride(1)
     p.kv = kv.data_ptr()
-    p.kv_stride_row = kv.stride(0) * (kv.element_size() if kv_format == SMLA_KV_FP8_E4M3 else 1)
+    p.kv_stride_row = kv.stride(0) * (kv.element_size() if kv_format != SMLA_KV_BF16 else 1)
     p.kv_format = kv_format
     p.indices, p.indices_stride_token = indices.data_ptr(), indices.stride(0)
     p.out, p.out_stride_token, p.out_stride_head = out.data_ptr(), out.stride(0), out.stride(1)

@@ -55,7 +55,8 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   if (p->s_kv < 1 || p->s_kv > 2147483647LL)
     return fail(SMLA_ERR_INVALID_ARGUMENT, "s_kv=%lld out of [1, 2^31-1]", (long long)p->s_kv);
   if (!std::isfinite(p->sm_scale)) return fail(SMLA_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
-  if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_E4M3)
+  if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_E4M3 &&
+      p->kv_format != SMLA_KV_FP4_E2M1)
     return fail(SMLA_ERR_INVALID_ARGUMENT, "kv_format=%d unknown", p->kv_format);
   if (p->b_topk != 0 && p->b_topk != 32 && p->b_topk != 64)
     return fail(SMLA_ERR_UNSUPPORTED, "b_topk=%d: supported 32, 64 (0 = auto)", p->b_topk);
@@ -92,10 +93,11 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
                     "kv_stride_row=%lld elements: need >= 576 and a multiple of 8",
                     (long long)p->kv_stride_row);
     } else {
-      if (p->kv_stride_row < SMLA_FP8_ROW_BYTES || p->kv_stride_row % 16)
+      const int row = p->kv_format == SMLA_KV_FP8_E4M3 ? SMLA_FP8_ROW_BYTES : SMLA_FP4_ROW_BYTES;
+      if (p->kv_stride_row < row || p->kv_stride_row % 16)
         return fail(SMLA_ERR_INVALID_ARGUMENT,
-                    "kv_stride_row=%lld bytes: need >= 640 and a multiple of 16",
-                    (long long)p->kv_stride_row);
+                    "kv_stride_row=%lld bytes: need >= %d and a multiple of 16",
+                    (long long)p->kv_stride_row, row);
     }
   }
 
@@ -103,8 +105,8 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   // B_TOPK 32 with a 4-deep gather ring measures faster than 64 with 2 stages;
   // the fp8 path is built for 32 only.
   pl.b_topk = p->b_topk ? p->b_topk : 32;
-  if (p->kv_format == SMLA_KV_FP8_E4M3 && pl.b_topk != 32)
-    return fail(SMLA_ERR_UNSUPPORTED, "fp8 KV supports b_topk 32 only");
+  if (p->kv_format != SMLA_KV_BF16 && pl.b_topk != 32)
+    return fail(SMLA_ERR_UNSUPPORTED, "quantised KV supports b_topk 32 only");
   const int32_t max_part = p->kv_format == SMLA_KV_FP8_E4M3 ? SMLA_MAX_SLOTS_PER_SPLIT_FP8
                                                             : SMLA_MAX_SLOTS_PER_SPLIT;
   const int32_t min_splits = (p->topk + max_part - 1) / max_part;
@@ -176,11 +178,13 @@ smla_status launch_plan(const smla_fwd_params* p, const Plan& pl, const int32_t*
   a.s_kv = p->s_kv;
   a.scale_log2 = p->sm_scale * 1.4426950408889634f;
   {
-    const int64_t row_len = p->kv_format == SMLA_KV_BF16 ? 2 * SMLA_D_QK : SMLA_FP8_ROW_BYTES;
+    const int64_t row_len = p->kv_format == SMLA_KV_BF16      ? 2 * SMLA_D_QK
+                            : p->kv_format == SMLA_KV_FP8_E4M3 ? SMLA_FP8_ROW_BYTES
+                                                               : SMLA_FP4_ROW_BYTES;
     const int64_t window = p->s_kv > 0 ? (p->s_kv - 1) * a.kv_row_bytes + row_len : 0;
     a.kv_window_bytes = window > 0 && window <= (int64_t)smla::kDummyOffset ? (uint32_t)window : 0u;
   }
-  const hipError_t e = smla::launch_fwd(a, pl.b_topk, p->kv_format == SMLA_KV_FP8_E4M3, stream);
+  const hipError_t e = smla::launch_fwd(a, pl.b_topk, p->kv_format, stream);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
 }
@@ -297,6 +301,28 @@ smla_status smla_pack_fp8_kv_host(const uint8_t* codes, const float* scales, int
     std::memcpy(row + SMLA_D_QK, scales + r * SMLA_FP8_NUM_GROUPS, SMLA_FP8_NUM_GROUPS * sizeof(float));
     std::memset(row + SMLA_D_QK + SMLA_FP8_NUM_GROUPS * sizeof(float), 0,
                 SMLA_FP8_ROW_BYTES - SMLA_D_QK - SMLA_FP8_NUM_GROUPS * sizeof(float));
+  }
+  return SMLA_OK;
+}
+
+smla_status smla_pack_fp4_kv_host(const uint8_t* codes, const float* scales, int64_t rows,
+                                  void* packed) {
+  if (rows < 0) return fail(SMLA_ERR_INVALID_ARGUMENT, "rows=%lld is negative", (long long)rows);
+  if (rows > 0 && (!codes || !scales || !packed))
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "a pointer is NULL");
+  for (int64_t i = 0; i < rows * SMLA_D_QK; ++i)
+    if (codes[i] > 15)
+      return fail(SMLA_ERR_INVALID_ARGUMENT, "code %d at element %lld is not a 4-bit code",
+                  (int)codes[i], (long long)i);
+  char* dst = static_cast<char*>(packed);
+  constexpr int kCodeBytes = SMLA_D_QK / 2;
+  for (int64_t r = 0; r < rows; ++r) {
+    unsigned char* row = reinterpret_cast<unsigned char*>(dst + r * SMLA_FP4_ROW_BYTES);
+    const uint8_t* c = codes + r * SMLA_D_QK;
+    for (int k = 0; k < kCodeBytes; ++k) row[k] = (unsigned char)(c[2 * k] | (c[2 * k + 1] << 4));
+    std::memcpy(row + kCodeBytes, scales + r * SMLA_FP8_NUM_GROUPS, SMLA_FP8_NUM_GROUPS * sizeof(float));
+    std::memset(row + kCodeBytes + SMLA_FP8_NUM_GROUPS * sizeof(float), 0,
+                SMLA_FP4_ROW_BYTES - kCodeBytes - SMLA_FP8_NUM_GROUPS * sizeof(float));
   }
   return SMLA_OK;
 }

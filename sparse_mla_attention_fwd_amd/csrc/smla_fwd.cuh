@@ -609,23 +609,65 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp8 KV cache.  A packed row is 576 E4M3 codes followed by five float32
-// scales (one per 128 columns) and padding to 640 bytes: a token's data and
-// scales sit side by side, as the page's section "Decoding KV Cache Layout 优化"
-// recommends, so one gather brings both.  Raw rows land in an LDS ring by
-// direct-to-LDS loads; the workgroup converts the codes of block i+1 to bf16
-// (exactly) in the stage layout above while computing block i, so the MFMA
-// code is shared, and folds the scales in fp32 (dequantisation without any
-// rounding of K or V).
-constexpr int kFp8RowChunks = kFp8RowBytes / 16;   // 40
+// Quantised KV caches: a packed row holds a token's 576 codes followed by five
+// float32 scales (one per 128 columns) and padding, data next to scale as the
+// page's section "Decoding KV Cache Layout 优化" recommends, so one gather
+// brings both.  Two code formats:
+//   fp8: OCP E4M3, one code per byte, 640-byte rows;
+//   fp4: OCP E2M1, two codes per byte (column 2k in the low nibble of byte k,
+//        column 2k+1 in the high nibble), 320-byte rows (the pages name an FP4
+//        KV cache for decode beside the FP8 one).
+// Raw rows land in an LDS ring by direct-to-LDS loads; the workgroup converts
+// the codes of block i+1 to bf16 (exactly: every E4M3 and every E2M1 value is
+// a bf16 value) in the stage layout above while computing block i, so the
+// MFMA code is shared, and folds the scales in fp32 (dequantisation without
+// any rounding of K or V).
+struct KvFp8Format {
+  static constexpr int ROW = kFp8RowBytes;        // 640
+  static constexpr int CODE_BYTES = kDqk;         // 576
+  static constexpr int MAX_SLOTS = kMaxSlotsPerSplitFp8;
+  // 16 codes of row r, columns 16cc .. 16cc+15 -> eight packed bf16 pairs
+  __device__ __forceinline__ static void convert16(const char* raw, int r, int cc, uint32_t (&o)[8]) {
+    const i32x4 codes = lds_load<i32x4>(raw, r * ROW + cc * 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // two codes -> two exact fp32 values -> two exact bf16 values
+      const auto f = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(codes[j >> 1], true)
+                             : __builtin_amdgcn_cvt_pk_f32_fp8(codes[j >> 1], false);
+      o[j] = pack2_bf16(f[0], f[1]);
+    }
+  }
+};
+struct KvFp4Format {
+  static constexpr int ROW = kFp4RowBytes;        // 320
+  static constexpr int CODE_BYTES = kDqk / 2;     // 288
+  static constexpr int MAX_SLOTS = kMaxSlotsPerSplit;
+  __device__ __forceinline__ static void convert16(const char* raw, int r, int cc, uint32_t (&o)[8]) {
+    const i32x2 codes = lds_load<i32x2>(raw, r * ROW + cc * 8);
+    static_for<0, 8>([&](auto J) __attribute__((always_inline)) {
+      // byte j%4 of word j/4: columns 2j (low nibble) and 2j+1 (high nibble),
+      // converted with scale 1 (exact)
+      constexpr int j = decltype(J)::value;
+      const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)codes[j >> 2], 1.0f, j & 3);
+      o[j] = __builtin_bit_cast(uint32_t, b);
+    });
+  }
+};
 
 // Gather of one block of packed rows into a raw LDS slot, row-major; wave
-// instruction k fills 64 consecutive 16-byte chunks (whole lines of ~2 rows).
-template <int NW, bool BUF>
-struct RawGatherFp8 {
+// instruction k fills 64 consecutive 16-byte chunks (whole lines of several
+// rows).  When the block's units do not divide evenly among the waves, a wave
+// past the last unit repeats its own previous unit (the same bytes to the
+// same LDS slot), so that every wave issues PER_WAVE instructions per block:
+// the waits count them.
+template <int NW, bool BUF, class Fmt>
+struct RawGather {
   static constexpr int BT = 32;
-  static constexpr int UNITS = BT * kFp8RowChunks / 64;   // 20 instructions per block
+  static constexpr int CHUNKS = Fmt::ROW / 16;                 // 16-byte chunks per row
+  static constexpr int UNITS = BT * CHUNKS / 64;              // fp8 20, fp4 10 instructions per block
+  static_assert(BT * CHUNKS % 64 == 0, "whole units per block");
   static constexpr int PER_WAVE = (UNITS + NW - 1) / NW;
+  static constexpr bool EARLY = false;
   KvSource<BUF> src;
   int64_t row_bytes;
   const int* sidx_blk;
@@ -642,17 +684,16 @@ struct RawGatherFp8 {
   }
   __device__ __forceinline__ void issue(int k) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-    const int u = k * NW + w;                              // wave-uniform
-    if (UNITS % NW == 0 || u < UNITS) {
-      const int c = u * 64 + l;
-      const int row = c / kFp8RowChunks, ch = c - row * kFp8RowChunks;
-      const int kvrow = sidx_blk[row];
-      if constexpr (BUF)
-        src.load16((LDS_AS void*)(slot + u * 1024), (uint32_t)kvrow * (uint32_t)row_bytes + (ch << 4),
-                   nullptr, 0);
-      else
-        src.load16((LDS_AS void*)(slot + u * 1024), 0, src.kv + (int64_t)kvrow * row_bytes + (ch << 4), 0);
-    }
+    int u = k * NW + w;                                    // wave-uniform
+    if (UNITS % NW != 0 && u >= UNITS) u -= NW;            // repeat this wave's previous unit
+    const int c = u * 64 + l;
+    const int row = c / CHUNKS, ch = c - row * CHUNKS;
+    const int kvrow = sidx_blk[row];
+    if constexpr (BUF)
+      src.load16((LDS_AS void*)(slot + u * 1024), (uint32_t)kvrow * (uint32_t)row_bytes + (ch << 4),
+                 nullptr, 0);
+    else
+      src.load16((LDS_AS void*)(slot + u * 1024), 0, src.kv + (int64_t)kvrow * row_bytes + (ch << 4), 0);
   }
   __device__ __forceinline__ void issue_all() {
 #pragma unroll
@@ -661,14 +702,14 @@ struct RawGatherFp8 {
 };
 
 // Conversion of one raw block into a bf16 stage: task c converts 16 codes of
-// row c/36 (columns 16·(c%36) .. +15).  Every E4M3 value is exactly a bf16
-// value, so the stage holds the codes without rounding; the row's group
-// scales are applied in fp32 by the block computation (to the QK partial sums
-// of each group, and to S for each V group).  The scales are copied to a
-// separate small tile: once converted, the raw slot may be refilled by any
-// wave while others still compute on the block.
-template <int NW>
-struct DequantFp8 {
+// row c/36 (columns 16·(c%36) .. +15).  The stage holds the codes without
+// rounding; the row's group scales are applied in fp32 by the block
+// computation (to the QK partial sums of each group, and to S for each V
+// group).  The scales are copied to a separate small tile: once converted,
+// the raw slot may be refilled by any wave while others still compute on the
+// block.
+template <int NW, class Fmt>
+struct DequantRaw {
   static constexpr int BT = 32;
   static constexpr int TASKS = BT * (kDqk / 16);            // 1152
   static constexpr int NT = NW * 64;
@@ -682,19 +723,12 @@ struct DequantFp8 {
     // Threads past the last task redo it: the same bytes written twice.
     const int c = min(k * NT + tid, TASKS - 1);
     const int r = c / 36, cc = c - r * 36;
-    const i32x4 codes = lds_load<i32x4>(raw, r * kFp8RowBytes + cc * 16);
     // every task also copies one scale of its row (groups repeat: same value)
     const int gs = cc % 5;
     *(LDS_AS float*)((LDS_AS char*)(LDS_AS void*)stile + (gs * BT + r) * 4) =
-        lds_load<float>(raw, r * kFp8RowBytes + kDqk + gs * 4);
+        lds_load<float>(raw, r * Fmt::ROW + Fmt::CODE_BYTES + gs * 4);
     uint32_t o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // two codes -> two exact fp32 values -> two exact bf16 values
-      const auto f = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(codes[j >> 1], true)
-                             : __builtin_amdgcn_cvt_pk_f32_fp8(codes[j >> 1], false);
-      o[j] = pack2_bf16(f[0], f[1]);
-    }
+    Fmt::convert16(raw, r, cc, o);
     // bf16 chunks 2cc and 2cc+1 of row r in the unit layout
     const int rb = r >> 3, r8 = r & 7;
 #pragma unroll
@@ -711,12 +745,12 @@ struct DequantFp8 {
   }
 };
 
-template <int NW, bool SPLIT, bool BUF>
+template <int NW, bool SPLIT, bool BUF, class Fmt = KvFp8Format>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   constexpr int BT = 32;
   constexpr int NSTR = 4;                                  // raw ring depth
-  constexpr int LPB = RawGatherFp8<NW, BUF>::PER_WAVE;
-  constexpr int RAW = BT * kFp8RowBytes;
+  constexpr int LPB = RawGather<NW, BUF, Fmt>::PER_WAVE;
+  constexpr int RAW = BT * Fmt::ROW;
   constexpr int TILE = BT * kRowBytesBf16;
   __shared__ __attribute__((aligned(1024))) char rw0[RAW];
   __shared__ __attribute__((aligned(1024))) char rw1[RAW];
@@ -726,7 +760,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char tl1[TILE];
   __shared__ __attribute__((aligned(16))) float sc0[5 * BT];
   __shared__ __attribute__((aligned(16))) float sc1[5 * BT];
-  __shared__ int sidx[kMaxSlotsPerSplitFp8 + BT];
+  __shared__ int sidx[Fmt::MAX_SLOTS + BT];
   __shared__ int swcnt[NW];
   char* const raws[4] = {rw0, rw1, rw2, rw3};
   char* const tiles[2] = {tl0, tl1};
@@ -758,7 +792,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
   for (int b = 0; b < NSTR; ++b) {
     if (b < nblk) {
-      RawGatherFp8<NW, BUF> rg;
+      RawGather<NW, BUF, Fmt> rg;
       rg.prepare(raws[b], src, a.kv_row_bytes, sidx + b * BT, tid);
       rg.issue_all();
     }
@@ -766,7 +800,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
   if (nblk > 0) {
     wait_block<LPB, NSTR>(min(nblk - 1, NSTR - 1));
     barrier_no_vm_drain();
-    DequantFp8<NW> dq{raws[0], tiles[0], stiles[0], tid};
+    DequantRaw<NW, Fmt> dq{raws[0], tiles[0], stiles[0], tid};
     dq.run_all();
   }
 
@@ -781,10 +815,10 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
     else
       wait_block<LPB, NSTR>(0);
     barrier_no_vm_drain();
-    RawGatherFp8<NW, BUF> rg;
+    RawGather<NW, BUF, Fmt> rg;
     if constexpr (decltype(REFILL)::value)
       rg.prepare(raws[s], src, a.kv_row_bytes, sidx + (i + NSTR) * BT, tid);
-    DequantFp8<NW> dq{raws[(s + 1) % NSTR], tiles[(s + 1) & 1], stiles[(s + 1) & 1], tid};
+    DequantRaw<NW, Fmt> dq{raws[(s + 1) % NSTR], tiles[(s + 1) & 1], stiles[(s + 1) & 1], tid};
     compute_block<NW, BT, decltype(REFILL)::value, decltype(DEQ)::value, true>(
         tiles[s & 1], lofs, qf, st, i, nvalid, a.scale_log2, lane, rg, dq, stiles[s & 1]);
   };
@@ -825,9 +859,10 @@ void launch_bf16_variant(const FwdArgs& a, hipStream_t stream) {
                      0, stream, a);
 }
 
-template <int NW, bool SPLIT, bool BUF>
+template <int NW, bool SPLIT, bool BUF, class Fmt = KvFp8Format>
 void launch_fp8_variant(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, SPLIT, BUF>), dim3(grid_size(a)), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((smla_fwd_fp8_kernel<NW, SPLIT, BUF, Fmt>), dim3(grid_size(a)), dim3(NW * 64), 0,
+                     stream, a);
 }
 
 }  // namespace

@@ -69,7 +69,6 @@ template <bool SPLIT, bool BUF, int NST>
 __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
   constexpr int NW = 4, BT = 32, KT = 2;
   constexpr int NP = 9;                       // 64-column windows of d_qk (pairs of MFMA steps)
-  constexpr int NG = 5;                       // scale groups of d_qk
   constexpr int NQ = NP * 2 * KT;             // QK MFMAs per block
   constexpr int NPV = 32;                     // PV MFMAs per block
   constexpr int LPB = 5;                      // gather instructions per wave per block

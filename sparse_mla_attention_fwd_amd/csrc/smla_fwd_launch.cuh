@@ -38,6 +38,18 @@ hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
 }
 
 template <int NW>
+hipError_t launch_fp4(const FwdArgs& a, hipStream_t stream) {
+  const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
+  if (split)
+    buf ? launch_fp8_variant<NW, true, true, KvFp4Format>(a, stream)
+        : launch_fp8_variant<NW, true, false, KvFp4Format>(a, stream);
+  else
+    buf ? launch_fp8_variant<NW, false, true, KvFp4Format>(a, stream)
+        : launch_fp8_variant<NW, false, false, KvFp4Format>(a, stream);
+  return hipGetLastError();
+}
+
+template <int NW>
 hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
   const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
   if constexpr (NW == 4) {

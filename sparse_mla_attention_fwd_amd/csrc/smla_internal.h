@@ -12,6 +12,7 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kRowBytesBf16 = kDqk * 2;   // 1152: nine 128-byte lines
 constexpr int kFp8RowBytes = 640;         // 576 codes + 5 float32 scales + pad
+constexpr int kFp4RowBytes = 320;         // 288 bytes of two codes each + 5 float32 scales + pad
 constexpr int kMaxSlotsPerSplit = 2048;
 // fp8 KV: the raw-row ring and two bf16 stages leave room for 1536 indices
 constexpr int kMaxSlotsPerSplitFp8 = 1536;
@@ -51,10 +52,12 @@ struct FwdArgs {
   uint32_t kv_window_bytes;
 };
 
-// Launch the forward pass (and the split combine when num_splits > 1).
-// fp8 selects the packed-fp8 KV producer.  Returns the HIP error of the
-// launches.
-hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream);
+// KV row formats (the values of smla_kv_format).
+enum KvFormat { kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2 };
+
+// Launch the forward pass (and the split combine when num_splits > 1) for a
+// KV row format.  Returns the HIP error of the launches.
+hipError_t launch_fwd(const FwdArgs& a, int b_topk, int kv_format, hipStream_t stream);
 
 // Paged KV: logical index -> physical row through each token's block table
 // (-1 when masked), written contiguously to phys [s_q, topk].
@@ -70,5 +73,7 @@ template <int NW, int BT>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream);
 template <int NW>
 hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream);
+template <int NW>
+hipError_t launch_fp4(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace smla

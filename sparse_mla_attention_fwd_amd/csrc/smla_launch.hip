@@ -92,10 +92,18 @@ hipError_t launch_paged_translate(const int32_t* idx, int64_t idx_st, const int3
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int b_topk, bool fp8, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a, int b_topk, int kv_format, hipStream_t stream) {
   hipError_t e;
   const bool b64 = b_topk == 64;
-  if (fp8) {
+  if (kv_format == kKvFp4) {
+    switch (a.h_q) {
+      case 16: e = launch_fp4<1>(a, stream); break;
+      case 32: e = launch_fp4<2>(a, stream); break;
+      case 64:
+      case 128: e = launch_fp4<4>(a, stream); break;   // 128: two head groups
+      default: return hipErrorInvalidValue;
+    }
+  } else if (kv_format == kKvFp8) {
     switch (a.h_q) {
       case 16: e = launch_fp8<1>(a, stream); break;
       case 32: e = launch_fp8<2>(a, stream); break;

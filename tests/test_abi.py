@@ -130,14 +130,17 @@ def test_workspace_required_for_split_plans():
 
 
 @pytest.mark.parametrize("name,splits", [("tiny", None), ("prefill", 1), ("causal", 1), ("decode", 4),
-                                         ("decode_fp8", None)])
+                                         ("decode_fp8", None), ("decode_fp4", None),
+                                         ("decode_paged", 4)])
 def test_plans_of_named_workloads(name, splits):
     import workloads
     w = workloads.WORKLOADS[name]
     fp8 = w.kv_format == "fp8"
+    fmt = {"bf16": 0, "fp8": 1, "fp4": 2}[w.kv_format]
     p = _params(s_q=w.s_q, h_q=w.h_q, topk=w.topk, s_kv=w.s_kv, num_splits=w.num_splits,
                 q_stride_token=w.h_q * 576, out_stride_token=w.h_q * 512, lse_stride_token=w.h_q,
-                indices_stride_token=w.topk, kv_format=int(fp8), kv_stride_row=640 if fp8 else 576)
+                indices_stride_token=w.topk, kv_format=fmt,
+                kv_stride_row={"bf16": 576, "fp8": 640, "fp4": 320}[w.kv_format])
     ns, bt = _lib.smla_fwd_plan(p)
     if splits is not None:
         assert ns == splits
@@ -220,3 +223,32 @@ def test_paged_workspace_and_null_paged():
     assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == _lib.SMLA_ERR_WORKSPACE
     p.s_q = 0
     assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == _lib.SMLA_OK
+
+
+def test_fp4_plan_limits_and_strides():
+    p = _params(kv_format=2, kv_stride_row=320, topk=2048, indices_stride_token=2048, num_splits=1)
+    assert _lib.smla_fwd_plan(p) == (1, 32)       # 2048 slots fit one fp4 part
+    p.b_topk = 64
+    with pytest.raises(_lib.SmlaError):
+        _lib.smla_fwd_plan(p)
+    p.b_topk = 0
+    for bad in (304, 328):                        # shorter than a row / not 16-byte aligned
+        p.kv_stride_row = bad
+        with pytest.raises(_lib.SmlaError):
+            _lib.smla_fwd_plan(p)
+
+
+def test_pack_fp4_rows_host():
+    rng = np.random.default_rng(1)
+    codes = torch.from_numpy(rng.integers(0, 16, (5, 576), dtype=np.uint8))
+    scales = torch.from_numpy(rng.random((5, 5), dtype=np.float32))
+    packed = _lib.smla_pack_fp4_kv_host(codes, scales)
+    assert packed.shape == (5, 320)
+    c = codes.numpy()
+    assert np.array_equal(packed[:, :288].numpy(), (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8))
+    assert torch.equal(packed[:, 288:308].contiguous().view(torch.float32), scales)
+    assert torch.all(packed[:, 308:] == 0)
+    bad = codes.clone()
+    bad[2, 7] = 16
+    with pytest.raises(_lib.SmlaError):
+        _lib.smla_pack_fp4_kv_host(bad, scales)

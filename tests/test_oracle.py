@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (RESCALE_THRES, dequant_fp8_rows, e4m3fn_decode, lse_combine,
+from oracle import (RESCALE_THRES, dequant_fp4_rows, dequant_fp8_rows, e2m1_decode, e4m3fn_decode,
+                    lse_combine,
                     sparse_mla_fwd_exact, sparse_mla_fwd_online, sparse_mla_fwd_split)
 from oracle.cost_model import cost_model_cycles
 from oracle.paged import sparse_mla_fwd_paged
@@ -387,3 +388,46 @@ def test_paged_unallocated_block_and_one_row():
     assert np.allclose(o[0], np.broadcast_to(v[:d_v], o[0].shape), rtol=0, atol=1e-13)
     x = float(np.float32(sc)) * (q[0] @ v)
     assert np.allclose(l[0], x + math.log(5), rtol=0, atol=1e-12)
+
+
+# ---- fp4 (OCP MX E2M1) KV-cache values
+
+def test_e2m1_decode_spec_values():
+    """The OCP MX specification's E2M1 figures: exponent bias 1, max normal
+    6.0, min normal 1.0, the one subnormal 0.5, signed zeros; the eight
+    magnitudes increase with the code and bit 3 is the sign."""
+    v = e2m1_decode(np.arange(16))
+    assert v[7] == 6.0 and v[2] == 1.0 and v[1] == 0.5 and v[0] == 0.0
+    assert np.array_equal(v[8:], -v[:8]) and np.signbit(v[8]) and not np.signbit(v[0])
+    assert np.all(np.diff(v[:8]) > 0)
+    assert sorted(set(np.abs(v).tolist())) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    with pytest.raises(ValueError):
+        e2m1_decode([16])
+
+
+def test_dequant_fp4_rows_groups():
+    codes = np.tile(np.arange(576) % 16, (2, 1))
+    scales = np.array([[1.0, 2.0, 4.0, 8.0, 0.25], [3.0, 3.0, 3.0, 3.0, 3.0]], dtype=np.float32)
+    v = dequant_fp4_rows(codes, scales)
+    for c in (0, 127, 128, 300, 511, 512, 575):
+        assert v[0, c] == e2m1_decode(codes[0, c]) * scales[0, c // 128]
+        assert v[1, c] == e2m1_decode(codes[1, c]) * 3.0
+
+
+def test_fp4_generator_rounds_to_nearest_grid_value():
+    """The fp4 workload quantiser: every dequantised element is the E2M1 grid
+    value nearest to value / scale (same draws regenerated here), and the
+    group maximum maps to +-6."""
+    x = workloads.make_random(s_q=1, h_q=16, topk=4, s_kv=64, seed=9, kv_format="fp4")
+    rng = np.random.default_rng(9)
+    rng.standard_normal((1, 16 * 576), dtype=np.float32)          # Q draws
+    raw = rng.standard_normal((64, 576), dtype=np.float32)
+    codes, scales = x["kv_codes"].numpy(), x["kv_scales"].numpy()
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    for g in range(5):
+        c0, c1 = 128 * g, min(576, 128 * (g + 1))
+        y = raw[:, c0:c1] / scales[:, g:g + 1]
+        got = e2m1_decode(codes[:, c0:c1])
+        err = np.abs(np.abs(y)[..., None] - grid).min(axis=-1)
+        assert np.allclose(np.abs(np.abs(y) - np.abs(got)), err, atol=1e-6)
+        assert np.all(np.abs(got).max(axis=1) == 6.0)

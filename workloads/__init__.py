@@ -22,6 +22,10 @@ to nearest even, torch's cast).  The five named workloads:
                   rows, the 32768 pages of the pool dealt to the 64 sequences in
                   a random order (each sequence's block table lists its 512
                   pages); indices are logical positions in [0, 32768).
+* ``decode_fp4``: as ``decode_fp8`` with an FP4 (E2M1) cache: one float32
+                  scale per 128-column group (scale = absmax / 6, code = the
+                  nearest E2M1 value of value / scale, ties to the even
+                  mantissa).
 * ``decode_fp8``: 128 sequences x 1 token, h_q 64, topk 2048, 16384 rows per
                   sequence, KV quantised to FP8 E4M3 with one float32 scale per
                   128-column group of each row (scale = absmax / 448, code =
@@ -43,6 +47,10 @@ D_QK = 576
 D_V = 512
 FP8_GROUP = 128
 FP8_MAX = 448.0
+FP4_MAX = 6.0
+# E2M1 magnitudes of codes 0..7 and the midpoints between neighbours
+_FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+_FP4_MID = (_FP4_GRID[1:] + _FP4_GRID[:-1]) / 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -56,7 +64,7 @@ class Workload:
     rows_per_seq: int = 0    # decode: KV rows per sequence
     causal: bool = False
     q_mult: float = 1.0
-    kv_format: str = "bf16"  # "bf16" or "fp8"
+    kv_format: str = "bf16"  # "bf16", "fp8" or "fp4"
     num_splits: int = 1      # split-topk parts the workload asks for (0: auto)
     page_size: int = 0       # paged KV: rows per page (0: not paged)
     seed: int = 0
@@ -89,6 +97,9 @@ WORKLOADS = {
     "decode_fp8": Workload("decode_fp8", s_q=128, h_q=64, topk=2048, s_kv=128 * 16384,
                            seqs=128, rows_per_seq=16384, kv_format="fp8", num_splits=0,
                            seed=5),
+    "decode_fp4": Workload("decode_fp4", s_q=128, h_q=64, topk=2048, s_kv=128 * 16384,
+                           seqs=128, rows_per_seq=16384, kv_format="fp4", num_splits=0,
+                           seed=7),
 }
 
 
@@ -124,6 +135,32 @@ def _normal_fp8_groups(rng: np.random.Generator, rows: int, cols: int,
             codes[r0:r1, c0:c1] = y.to(torch.float8_e4m3fn).view(torch.uint8)
             scales[r0:r1, g] = sc
     return codes, scales
+
+
+def _normal_fp4_groups(rng: np.random.Generator, rows: int, cols: int,
+                       chunk_rows: int = 1 << 16):
+    """N(0,1) float32 rows quantised per 128-column group to E2M1 codes (one
+    4-bit code per byte: bit 3 sign, bits 2..0 the magnitude index) plus a
+    float32 scale per group (scale = absmax / 6); the code is the nearest E2M1
+    value of value / scale, ties to the even mantissa."""
+    ng = -(-cols // FP8_GROUP)
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty((rows, ng), dtype=np.float32)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        x = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
+        for g in range(ng):
+            c0, c1 = g * FP8_GROUP, min(cols, (g + 1) * FP8_GROUP)
+            xs = x[:, c0:c1]
+            amax = np.abs(xs).max(axis=1)
+            sc = np.where(amax > 0, amax / np.float32(FP4_MAX), np.float32(1.0)).astype(np.float32)
+            a = np.minimum(np.abs(xs / sc[:, None]).astype(np.float64), FP4_MAX)
+            mag = np.searchsorted(_FP4_MID, a, side="left")          # nearest; a tie takes the lower
+            tie_up = (mag < 7) & (a == _FP4_MID[np.minimum(mag, 6)]) & (mag % 2 == 1)
+            mag = (mag + tie_up).astype(np.uint8)                    # ties to the even mantissa
+            codes[r0:r1, c0:c1] = mag | np.where((xs < 0) & (mag > 0), 8, 0).astype(np.uint8)
+            scales[r0:r1, g] = sc
+    return torch.from_numpy(codes), torch.from_numpy(scales)
 
 
 def _indices(rng: np.random.Generator, w: Workload) -> np.ndarray:
@@ -166,8 +203,11 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> dict:
     out = {"workload": w, "q": q, "sm_scale": w.sm_scale, "d_v": D_V}
     if w.kv_format == "fp8":
         out["kv_codes"], out["kv_scales"] = _normal_fp8_groups(rng, w.s_kv, D_QK)
+    elif w.kv_format == "fp4":
+        out["kv_codes"], out["kv_scales"] = _normal_fp4_groups(rng, w.s_kv, D_QK)
     else:
         out["kv"] = _normal_bf16(rng, (w.s_kv, D_QK))
+    out["kv_format"] = w.kv_format
     out["indices"] = torch.from_numpy(_indices(rng, w))
     if w.page_size:
         # the pool's pages dealt to the sequences in a random order
@@ -192,9 +232,12 @@ def make_random(*, s_q: int, h_q: int, topk: int, s_kv: int, seed: int,
     q = _normal_bf16(rng, (s_q, h_q, d_qk))
     if q_mult != 1.0:
         q = (q.float() * q_mult).to(torch.bfloat16)
-    res = {"q": q, "sm_scale": float(np.float32(1.0 / math.sqrt(d_qk))), "d_v": D_V}
+    res = {"q": q, "sm_scale": float(np.float32(1.0 / math.sqrt(d_qk))), "d_v": D_V,
+           "kv_format": kv_format}
     if kv_format == "fp8":
         res["kv_codes"], res["kv_scales"] = _normal_fp8_groups(rng, s_kv, d_qk)
+    elif kv_format == "fp4":
+        res["kv_codes"], res["kv_scales"] = _normal_fp4_groups(rng, s_kv, d_qk)
     else:
         res["kv"] = _normal_bf16(rng, (s_kv, d_qk))
     idx = np.empty((s_q, topk), dtype=np.int64)
