@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 3
+#define SMLA_ABI_VERSION 4
 
 /* The MLA shapes the kernels are built for: the query/key width d_qk is the
  * 512-wide latent plus the 64-wide rotary part, and V is the first 512 KV
@@ -188,6 +188,30 @@ smla_status smla_fwd_paged_workspace_size(const smla_fwd_params* p, const smla_p
  * aligned).  Validation and error behaviour as smla_fwd, plus the block table
  * (non-NULL when s_q > 0, 4-byte aligned) and the page geometry. */
 smla_status smla_fwd_paged(const smla_fwd_params* p, const smla_paged_kv* paged, void* stream);
+
+/* ---- Shape-dependent plan selection.
+ *
+ * The planner's choice (num_splits = b_topk = 0) follows measured behaviour
+ * on the named workloads; for other shapes a caller can time the candidate
+ * plans on its own inputs once and pass the winner explicitly (the library
+ * keeps no state).  Candidates: the planner's plan, then num_splits in
+ * {1, 2, 3, 4, 6, 8, 12, 16, 24, 32} with b_topk 32 and 64 (bf16 KV) or 32
+ * (fp8/fp4 KV), each valid distinct plan once. */
+
+/* Bytes of workspace smla_fwd_tune needs: the largest over the candidates. */
+smla_status smla_fwd_tune_workspace_size(const smla_fwd_params* p, size_t* bytes);
+
+/* Run every candidate plan (one warm-up launch, then `iterations` timed
+ * launches between two HIP events on `stream`) and return the fastest plan's
+ * num_splits and b_topk and its time per launch in microseconds (may be
+ * NULL).  The call BLOCKS until the timed work is done; it creates and
+ * destroys two HIP events and allocates no device memory.  Writes out and
+ * lse (the result of the last candidate, a correct forward pass) and uses
+ * p->workspace (smla_fwd_tune_workspace_size bytes, 256-byte aligned).
+ * iterations in [1, 1000].  p->num_splits and p->b_topk are ignored.  Flat
+ * KV only (for a paged cache, tune on the translated layout). */
+smla_status smla_fwd_tune(const smla_fwd_params* p, void* stream, int32_t iterations,
+                          int32_t* num_splits, int32_t* b_topk, float* microseconds);
 
 /* Host helper: pack E4M3 codes [rows, 576] and float32 scales [rows, 5]
  * (host memory, row-major, contiguous) into 640-byte fp8 KV rows at `packed`

@@ -21,12 +21,14 @@ import torch
 from . import _lib
 from ._lib import (D_QK, D_V, FP4_ROW_BYTES, FP8_ROW_BYTES, SMLA_KV_BF16, SMLA_KV_FP4_E2M1,  # noqa: F401
                    SMLA_KV_FP8_E4M3, SmlaError, make_paged, make_params, smla_fwd, smla_fwd_paged,
-                   smla_fwd_paged_workspace_size, smla_fwd_plan, smla_fwd_workspace_size,
-                   smla_pack_fp4_kv_host, smla_pack_fp8_kv_host)
+                   smla_fwd_paged_workspace_size, smla_fwd_plan, smla_fwd_tune,
+                   smla_fwd_tune_workspace_size, smla_fwd_workspace_size, smla_pack_fp4_kv_host,
+                   smla_pack_fp8_kv_host)
 
 __all__ = ["sparse_mla_fwd", "pack_fp8_kv", "pack_fp4_kv", "smla_fwd", "smla_fwd_plan",
            "smla_fwd_workspace_size", "smla_fwd_paged", "smla_fwd_paged_workspace_size",
-           "smla_pack_fp8_kv_host", "smla_pack_fp4_kv_host", "SmlaError"]
+           "smla_fwd_tune", "smla_fwd_tune_workspace_size", "tune_plan", "smla_pack_fp8_kv_host",
+           "smla_pack_fp4_kv_host", "SmlaError"]
 
 
 def pack_fp8_kv(codes: torch.Tensor, scales: torch.Tensor, device=None) -> torch.Tensor:
@@ -42,6 +44,22 @@ def pack_fp4_kv(codes: torch.Tensor, scales: torch.Tensor, device=None) -> torch
     ``device``."""
     packed = smla_pack_fp4_kv_host(codes.cpu(), scales.cpu())
     return packed.to(device) if device is not None else packed
+
+
+def tune_plan(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float, *,
+              kv_format: str = "bf16", iterations: int = 10) -> tuple[int, int, float]:
+    """Time the library's candidate plans on these inputs (smla_fwd_tune) and
+    return ``(num_splits, b_topk, microseconds)`` of the fastest; pass the
+    first two to ``sparse_mla_fwd``.  Blocks until the timing is done."""
+    fmt = {"bf16": SMLA_KV_BF16, "fp8": SMLA_KV_FP8_E4M3, "fp4": SMLA_KV_FP4_E2M1}[kv_format]
+    s_q, h_q, _ = q.shape
+    out = torch.empty((s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((s_q, h_q), dtype=torch.float32, device=q.device)
+    p = make_params(q, kv, indices, sm_scale, out, lse, kv_format=fmt)
+    need = smla_fwd_tune_workspace_size(p)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p.workspace, p.workspace_bytes = ws.data_ptr(), ws.numel()
+    return smla_fwd_tune(p, iterations)
 
 
 def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float,

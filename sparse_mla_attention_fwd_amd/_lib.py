@@ -33,9 +33,9 @@ MAX_SLOTS_PER_SPLIT_FP8 = 1536
 
 # Every symbol include/smla.h declares.
 EXPORTS = ("smla_fwd_plan", "smla_fwd_workspace_size", "smla_fwd", "smla_fwd_paged_workspace_size",
-           "smla_fwd_paged", "smla_pack_fp8_kv_host", "smla_pack_fp4_kv_host", "smla_status_string",
-           "smla_last_error", "smla_abi_version")
-ABI_VERSION = 3
+           "smla_fwd_paged", "smla_fwd_tune_workspace_size", "smla_fwd_tune", "smla_pack_fp8_kv_host",
+           "smla_pack_fp4_kv_host", "smla_status_string", "smla_last_error", "smla_abi_version")
+ABI_VERSION = 4
 
 
 class smla_fwd_params(ctypes.Structure):
@@ -90,6 +90,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.smla_fwd_paged_workspace_size.restype = ctypes.c_int
     lib.smla_fwd_paged.argtypes = [P, G, ctypes.c_void_p]
     lib.smla_fwd_paged.restype = ctypes.c_int
+    lib.smla_fwd_tune_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.smla_fwd_tune_workspace_size.restype = ctypes.c_int
+    I32 = ctypes.POINTER(ctypes.c_int32)
+    lib.smla_fwd_tune.argtypes = [P, ctypes.c_void_p, ctypes.c_int32, I32, I32, ctypes.POINTER(ctypes.c_float)]
+    lib.smla_fwd_tune.restype = ctypes.c_int
     lib.smla_pack_fp8_kv_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.smla_pack_fp8_kv_host.restype = ctypes.c_int
     lib.smla_pack_fp4_kv_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
@@ -147,6 +152,23 @@ def smla_fwd_paged(params: smla_fwd_params, paged: smla_paged_kv, stream: int | 
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
     _check(load().smla_fwd_paged(ctypes.byref(params), ctypes.byref(paged), ctypes.c_void_p(stream)))
+
+
+def smla_fwd_tune_workspace_size(params: smla_fwd_params) -> int:
+    n = ctypes.c_size_t()
+    _check(load().smla_fwd_tune_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def smla_fwd_tune(params: smla_fwd_params, iterations: int = 10,
+                  stream: int | None = None) -> tuple[int, int, float]:
+    """Time the candidate plans; returns (num_splits, b_topk, microseconds)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    ns, bt, us = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_float()
+    _check(load().smla_fwd_tune(ctypes.byref(params), ctypes.c_void_p(stream), int(iterations),
+                                ctypes.byref(ns), ctypes.byref(bt), ctypes.byref(us)))
+    return ns.value, bt.value, us.value
 
 
 def make_paged(block_table: torch.Tensor, page_size: int) -> smla_paged_kv:

@@ -211,6 +211,31 @@ smla_status check_paged(const smla_fwd_params* p, const smla_paged_kv* pg) {
   return SMLA_OK;
 }
 
+// Candidate plans for smla_fwd_tune: the planner's own plan first, then the
+// split counts below with each supported block size, every valid plan once.
+int tune_candidates(const smla_fwd_params* p, Plan* out, int maxn) {
+  static const int32_t kSplits[] = {0, 1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+  const int32_t bts[2] = {32, 64};
+  const int nbt = p->kv_format == SMLA_KV_BF16 ? 2 : 1;
+  int n = 0;
+  for (int32_t ns : kSplits) {
+    for (int b = 0; b < nbt; ++b) {
+      smla_fwd_params q = *p;
+      q.num_splits = ns;
+      q.b_topk = bts[b];
+      Plan pl;
+      if (check_and_plan(&q, &pl) != SMLA_OK) continue;
+      bool seen = false;
+      for (int i = 0; i < n; ++i)
+        seen |= out[i].num_splits == pl.num_splits && out[i].b_topk == pl.b_topk;
+      if (!seen && n < maxn) out[n++] = pl;
+    }
+  }
+  g_last_error[0] = 0;   // rejected candidates are not a failure of the call
+  return n;
+}
+constexpr int kMaxTuneCandidates = 32;
+
 // Bytes of the translated-index region at the start of a paged workspace.
 size_t translated_bytes(const smla_fwd_params* p) {
   return ((size_t)p->s_q * (size_t)p->topk * sizeof(int32_t) + 255) & ~size_t(255);
@@ -287,6 +312,79 @@ smla_status smla_fwd_paged(const smla_fwd_params* p, const smla_paged_kv* pg, vo
       pg->table_width, pg->page_size, p->s_kv / pg->page_size, p->s_q, p->topk, phys, st);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return launch_plan(p, pl, phys, p->topk, static_cast<char*>(p->workspace) + tb, st);
+}
+
+smla_status smla_fwd_tune_workspace_size(const smla_fwd_params* p, size_t* bytes) {
+  if (!bytes) return fail(SMLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan base;
+  const smla_status s = check_and_plan(p, &base);
+  if (s != SMLA_OK) return s;
+  Plan c[kMaxTuneCandidates];
+  const int n = tune_candidates(p, c, kMaxTuneCandidates);
+  size_t need = base.workspace_bytes;
+  for (int i = 0; i < n; ++i) need = c[i].workspace_bytes > need ? c[i].workspace_bytes : need;
+  *bytes = need;
+  return SMLA_OK;
+}
+
+smla_status smla_fwd_tune(const smla_fwd_params* p, void* stream, int32_t iterations,
+                          int32_t* num_splits, int32_t* b_topk, float* microseconds) {
+  if (!num_splits || !b_topk)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "num_splits and b_topk outputs must not be NULL");
+  if (iterations < 1 || iterations > 1000)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "iterations=%d outside [1, 1000]", iterations);
+  Plan base;
+  smla_status s = check_and_plan(p, &base);
+  if (s != SMLA_OK) return s;
+  Plan c[kMaxTuneCandidates];
+  const int n = tune_candidates(p, c, kMaxTuneCandidates);
+  size_t need = base.workspace_bytes;
+  for (int i = 0; i < n; ++i) need = c[i].workspace_bytes > need ? c[i].workspace_bytes : need;
+  if (p->s_q == 0 || n == 0) {
+    *num_splits = base.num_splits;
+    *b_topk = base.b_topk;
+    if (microseconds) *microseconds = 0.f;
+    return SMLA_OK;
+  }
+  if (need && (!p->workspace || p->workspace_bytes < need))
+    return fail(SMLA_ERR_WORKSPACE, "workspace of %zu bytes needed for the candidates, %zu given",
+                need, p->workspace ? p->workspace_bytes : (size_t)0);
+  if (need && reinterpret_cast<uintptr_t>(p->workspace) % 256)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(SMLA_ERR_HIP, "hipEventCreate failed");
+  }
+  float best = -1.f;
+  int best_i = 0;
+  for (int i = 0; i < n && s == SMLA_OK; ++i) {
+    s = launch_plan(p, c[i], p->indices, p->indices_stride_token, static_cast<char*>(p->workspace), st);
+    if (s != SMLA_OK) break;                                    // warm-up launch
+    if (hipEventRecord(e0, st) != hipSuccess) { s = fail(SMLA_ERR_HIP, "hipEventRecord failed"); break; }
+    for (int k = 0; k < iterations && s == SMLA_OK; ++k)
+      s = launch_plan(p, c[i], p->indices, p->indices_stride_token, static_cast<char*>(p->workspace), st);
+    if (s != SMLA_OK) break;
+    float ms = 0.f;
+    if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      s = fail(SMLA_ERR_HIP, "timing a candidate plan failed");
+      break;
+    }
+    const float us = ms * 1000.f / iterations;
+    if (best < 0.f || us < best) {
+      best = us;
+      best_i = i;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (s != SMLA_OK) return s;
+  *num_splits = c[best_i].num_splits;
+  *b_topk = c[best_i].b_topk;
+  if (microseconds) *microseconds = best;
+  return SMLA_OK;
 }
 
 smla_status smla_pack_fp8_kv_host(const uint8_t* codes, const float* scales, int64_t rows,

@@ -252,3 +252,27 @@ def test_pack_fp4_rows_host():
     bad[2, 7] = 16
     with pytest.raises(_lib.SmlaError):
         _lib.smla_pack_fp4_kv_host(bad, scales)
+
+
+def test_tune_arguments_and_workspace():
+    lib = _lib.load()
+    p = _params(h_q=128, q_stride_token=128 * 576, out_stride_token=128 * 512, lse_stride_token=128,
+                topk=512, indices_stride_token=512)
+    need = _lib.smla_fwd_tune_workspace_size(p)
+    # at least the workspace of every explicit split count it tries
+    for ns in (1, 2, 4, 8, 16, 32):
+        p.num_splits = ns
+        assert need >= _lib.smla_fwd_workspace_size(p)
+    ns, bt, us = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_float()
+    args = (ctypes.byref(ns), ctypes.byref(bt), ctypes.byref(us))
+    # rejected on the host before any HIP call
+    assert lib.smla_fwd_tune(ctypes.byref(p), None, 0, *args) == _lib.SMLA_ERR_INVALID_ARGUMENT
+    assert lib.smla_fwd_tune(ctypes.byref(p), None, 10, None, ctypes.byref(bt), None) == \
+        _lib.SMLA_ERR_INVALID_ARGUMENT
+    assert lib.smla_fwd_tune(ctypes.byref(p), None, 10, *args) == _lib.SMLA_ERR_WORKSPACE
+    bad = _params(h_q=24)
+    assert lib.smla_fwd_tune(ctypes.byref(bad), None, 10, *args) == _lib.SMLA_ERR_UNSUPPORTED
+    # nothing to time: the planner's plan, no HIP call
+    empty = _params(s_q=0, q=0, kv=0, indices=0, out=0, lse=0)
+    assert lib.smla_fwd_tune(ctypes.byref(empty), None, 10, *args) == _lib.SMLA_OK
+    assert (ns.value, bt.value) == _lib.smla_fwd_plan(empty)

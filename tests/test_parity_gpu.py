@@ -357,3 +357,17 @@ def test_h128_short_splits_one_row_is_bit_exact(dev):
         assert np.array_equal(out[t], np.broadcast_to(v, out[t].shape)), f"row {r} not exact"
         xr = (workloads.to_f64(x["q"][t]) @ workloads.to_f64(x["kv"][r])) * x["sm_scale"]
         assert np.abs(lse[t] - (xr + math.log(512))).max() < 1e-4
+
+
+def test_tuned_plan_is_a_valid_plan_and_matches_the_oracle(dev):
+    """smla_fwd_tune times the candidate plans on a decode-like shape; the
+    outputs it leaves and those of the chosen plan both meet the parity bar."""
+    device, smla = dev
+    x = workloads.make_random(s_q=16, h_q=128, topk=512, s_kv=20000, seed=31, invalid_frac=0.1)
+    q, kv, idx = x["q"].to(device), x["kv"].to(device), x["indices"].to(device)
+    ns, bt, us = smla.tune_plan(q, kv, idx, x["sm_scale"], iterations=3)
+    assert bt in (32, 64) and 1 <= ns <= 512 and us > 0
+    _say(f"  tuned plan: num_splits={ns} b_topk={bt} ({us:.1f} us)")
+    out, lse = run_gpu(dev, x, num_splits=ns, b_topk=bt)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"tuned ns={ns} B{bt}")
