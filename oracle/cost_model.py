@@ -9,7 +9,7 @@ cycles are the bytes of Q and O (h_q * d * 2 * 2) plus the gathered KV
 
 The page prints this model's output for its own chip; the golden fixture
 ``tests/golden/ascend_cost_model.txt`` holds that printed table.  The same
-model, with MI355X constants, is how the repository's design notes judge
+model, with MI355X constants, is how the repository's design notes assess
 which unit bounds the kernel.
 """
 from __future__ import annotations
