@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--b-topk", type=int, default=0)
     ap.add_argument("--num-splits", type=int, default=-1, help="-1: the workload's own setting")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 skips")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -217,13 +219,26 @@ def main():
 
     def step():
         if w.page_size:
-            smla.smla_fwd_paged(p, paged, stream.cuda_stream)
+            smla.smla_fwd_paged(p, paged, torch.cuda.current_stream().cuda_stream)
         else:
-            smla.smla_fwd(p, stream.cuda_stream)
+            smla.smla_fwd(p, torch.cuda.current_stream().cuda_stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        # one step captured once (torch captures on a side stream) and
+        # replayed on the current stream: the host cost of a step becomes one
+        # graph launch
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+        def step():
+            graph.replay()
+        step()
+        torch.cuda.synchronize()
 
     # per-launch durations with events on the launch stream
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -273,7 +288,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "s_q": w.s_q, "h_q": w.h_q, "topk": w.topk, "s_kv": w.s_kv,
                    "d_qk": 576, "d_v": 512, "kv_format": fmt, "num_splits": plan_splits,
-                   "page_size": w.page_size or None,
+                   "page_size": w.page_size or None, "hip_graph": bool(args.graph),
                    "b_topk": plan_bt, "parallelism": "single GPU"},
         "roofline": roofline,
         "gather": {"bytes_per_launch": gathered, "GB/s": round(gathered / avg_launch_s / 1e9, 1),
