@@ -102,10 +102,8 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   }
 
   Plan pl{};
-  // B_TOPK 32 with a 4-deep gather ring measures faster than 64 with 2 stages;
-  // the fp8 path is built for 32 only.
-  pl.b_topk = p->b_topk ? p->b_topk : 32;
-  if (p->kv_format != SMLA_KV_BF16 && pl.b_topk != 32)
+  // The quantised-KV paths are built for B_TOPK 32 only.
+  if (p->kv_format != SMLA_KV_BF16 && p->b_topk != 0 && p->b_topk != 32)
     return fail(SMLA_ERR_UNSUPPORTED, "quantised KV supports b_topk 32 only");
   const int32_t max_part = p->kv_format == SMLA_KV_FP8_E4M3 ? SMLA_MAX_SLOTS_PER_SPLIT_FP8
                                                             : SMLA_MAX_SLOTS_PER_SPLIT;
@@ -129,6 +127,13 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   pl.slots_per_split = (p->topk + ns - 1) / ns;
   // the parts actually used may be fewer than ns after rounding up
   pl.num_splits = (p->topk + pl.slots_per_split - 1) / pl.slots_per_split;
+  // Block size: long splits (the pipelined 64-head kernel, from 1024 slots)
+  // and quantised KV run B_TOPK 32; short bf16 splits of 64-head workgroups
+  // run 64 (measured on the 128-head decode workload: 35.1 vs 39.5 us with
+  // 2 splits, 44.0 vs 47.4 us with 4).
+  pl.b_topk = p->b_topk ? p->b_topk
+                        : (p->kv_format == SMLA_KV_BF16 && p->h_q >= 64 && pl.slots_per_split < 1024) ? 64
+                                                                                                      : 32;
   if ((int64_t)p->s_q * pl.num_splits * (p->h_q > 64 ? 2 : 1) + 8 > 2147483647LL)
     return fail(SMLA_ERR_UNSUPPORTED, "grid of s_q*num_splits workgroups is too large");
   pl.workspace_bytes = 0;
