@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float xa0[NW * 16];
   __shared__ __attribute__((aligned(16))) float xa1[NW * 16];
   __shared__ __attribute__((aligned(16))) int ring[NST][NW * 64];   // index ring (as in the bf16 kernel)
-  __shared__ __attribute__((aligned(16))) uint32_t vmask[NST];
+  __shared__ __attribute__((aligned(16))) float vbias[NST][BT];   // per stage: 0 (valid slot) or -inf
   __shared__ float lsh[NW * 16];
   __shared__ int sred[4];
   char* const stages[6] = {st0, st1, st2, st3, st4, st5};
@@ -182,8 +182,12 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
       gt.voff = b < nblk ? (uint32_t)row * (uint32_t)a.kv_row_bytes + (uint32_t)(c << 4) : kDummyOffset;
     else
       gt.base = a.kv + (int64_t)row * a.kv_row_bytes + (c << 4);
-    const uint32_t bits = (uint32_t)__ballot(valid) & 0xFFu;
-    if (lane == 0) *((LDS_AS uint8_t*)(LDS_AS void*)vmask + s * 4 + w) = (uint8_t)bits;
+    if (lane < 8) vbias[s][8 * w + lane] = valid ? 0.f : kNegInf;   // lanes 0..7: rows 8w..8w+7
+  };
+  // score biases of keys 16kt + 4g + r of stage s
+  auto load_bias = [&](int s, f32x4 (&bias)[KT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) bias[kt] = lds_load<f32x4>((const char*)&vbias[s][0], (16 * kt + 4 * g) * 4);
   };
   auto issue = [&](const Gather& gt, char* stage, int m) __attribute__((always_inline)) {
     src.load16((LDS_AS void*)(stage + fp8_unit(m, w) * 1024), gt.voff, gt.base, 128 * m);
@@ -266,18 +270,16 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
   // step 5 also publishes the block's S operands (one per V group) and
   // rescale factors into exchange buffer p, early enough for the writes to
   // land while the remaining PV MFMAs run
-  auto soft_step = [&](auto K, Soft& sm, const QkOut& qo, uint32_t vm, const f32x4 (&sc4)[KT][4],
+  auto soft_step = [&](auto K, Soft& sm, const QkOut& qo, const f32x4 (&bias)[KT], const f32x4 (&sc4)[KT][4],
                        int p) __attribute__((always_inline)) {
     constexpr int k = decltype(K)::value;
     if constexpr (k == 0) {
-      const uint32_t vmg = vm >> (4 * g);   // validity of keys 4g + (16kt + r)
+      // an invalid slot's bias of -inf masks it; a valid slot's 0 changes nothing
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = fmaf(qo.sc4g[kt][r], qo.acc[kt][r], qo.p[kt][r]) * a.scale_log2;
-          sm.x[kt][r] = (vmg >> (16 * kt + r)) & 1u ? v : kNegInf;
-        }
+        for (int r = 0; r < 4; ++r)
+          sm.x[kt][r] = __builtin_fmaf(fmaf(qo.sc4g[kt][r], qo.acc[kt][r], qo.p[kt][r]), a.scale_log2, bias[kt][r]);
       float c = sm.x[0][0];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
@@ -296,13 +298,12 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
       st.running_max_for_softmax = sm.any ? rmax : st.running_max_for_softmax;
       st.sumexp *= sm.alpha;
     } else if constexpr (k == 3 || k == 4) {
+      // a masked slot weighs exp2(-inf) = 0; while the running max is -inf
+      // every score of the head is -inf and any finite offset gives zeros
       constexpr int kt = k - 3;
-      const float m = st.running_max_for_softmax;
+      const float m = st.running_max_for_softmax == kNegInf ? 0.f : st.running_max_for_softmax;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float xv = sm.x[kt][r];
-        sm.x[kt][r] = xv == kNegInf ? 0.f : __builtin_amdgcn_exp2f(xv - m);
-      }
+      for (int r = 0; r < 4; ++r) sm.x[kt][r] = __builtin_amdgcn_exp2f(sm.x[kt][r] - m);
     } else if constexpr (k == 5) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
@@ -353,11 +354,12 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
     barrier_no_vm_drain();
     QkOut qo;
     qk(st0, qo, [&](auto) {});
-    const uint32_t vm = lds_load<uint32_t>((const char*)vmask, 0);
+    f32x4 bias[KT];
+    load_bias(0, bias);
     f32x4 sc4[KT][4];
     read_scales(st0, sc4);
     Soft sm;
-    static_for<0, NSOFT>([&](auto K) __attribute__((always_inline)) { soft_step(K, sm, qo, vm, sc4, 0); });
+    static_for<0, NSOFT>([&](auto K) __attribute__((always_inline)) { soft_step(K, sm, qo, bias, sc4, 0); });
   }
 
   // ---- iteration i: consume S(i); QKᵀ(i+1); PV(i) with softmax(i+1); refill
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
 
     bf16x8 sop[NW];
     float alph[NW];
-    uint32_t vm = 0;
+    f32x4 bias[KT];
     f32x4 sc4[KT][4];
     constexpr int sn = (s + 1) % NST;         // stage of block i+1
     auto consume_reads = [&]() __attribute__((always_inline)) {
@@ -402,7 +404,6 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
         sop[ht] = lds_load<bf16x8>(xss[p], ((w * NW + ht) * 64 + lane) * 16);
         alph[ht] = lds_load<float>((const char*)xas[p], (ht * 16 + n) * 4);
       }
-      vm = lds_load<uint32_t>((const char*)vmask, sn * 4);
     };
     const char* const tile = stages[s];
     i32x2 vraw[PFV];
@@ -416,6 +417,7 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
       qk(stages[sn], qo, [&](auto I) __attribute__((always_inline)) {
         constexpr int q = decltype(I)::value;
         if constexpr (q == 0) consume_reads();
+        if constexpr (q == NQ - 4) load_bias(sn, bias);   // shortly before the softmax of block i+1
         if constexpr (q >= NQ - 8 && (q - (NQ - 8)) % 2 == 0) fetch_v((q - (NQ - 8)) / 2);
         dma_at(I);
       });
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
         if (next) read_scales(stages[sn], sc4);   // V-group scales for step 5
       }
       if constexpr (c % 3 == 1 && c / 3 < NSOFT) {
-        if (next) soft_step(std::integral_constant<int, c / 3>{}, sm, qo, vm, sc4, p ^ 1);
+        if (next) soft_step(std::integral_constant<int, c / 3>{}, sm, qo, bias, sc4, p ^ 1);
       }
       dma_at(std::integral_constant<int, NQ + c>{});
       __builtin_amdgcn_sched_barrier(0);

@@ -25,8 +25,8 @@
 //    its own object) rather than in registers keeps the compiler from
 //    placing waits of its own for them.
 //    Invalid slots gather the split's first valid row and are masked through
-//    a per-block validity word; blocks past the split's last valid slot are
-//    skipped.
+//    a per-block array of score biases (0 or -inf, added in the same fma that
+//    scales the score); blocks past the split's last valid slot are skipped.
 //  * Every iteration issues the same memory instructions: the gathers of a
 //    block past the split are dummies (buffer loads outside the KV window,
 //    which the hardware drops; with 64-bit addresses, loads of the padding
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
   // index ring: slot r, lane l of wave w at [r][w·64 + l] holds the index of
   // its block's row 8w + l%8
   __shared__ __attribute__((aligned(16))) int ring[4][NW * 64];
-  __shared__ __attribute__((aligned(16))) uint32_t vmask[4];   // per stage: slot validity bits
+  __shared__ __attribute__((aligned(16))) float vbias[4][BT];   // per stage: 0 (valid slot) or -inf
   __shared__ float lsh[NW * 16];
   __shared__ int sred[4];
   char* const stages[4] = {st0, st1, st2, st3};
@@ -191,12 +191,16 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
     return lds_read_opaque<decltype(R)::value * NW * 64 * 4>(ring_lane);
   };
   // Prepare the gather of block b into stage s from the loaded index raw
-  // (slots past the split are invalid), publishing the validity bits.
+  // (slots past the split are invalid), publishing the score biases.
   auto prepare_gather = [&](RowGather<BUF>& rg, int s, int b, int raw) __attribute__((always_inline)) {
     const int j = lo + b * BT + 8 * w + (lane & 7);
     const bool valid = rg.prepare(src, a.kv_row_bytes, j < hi ? raw : -1, sc.pad_row, a.s_kv, lane, b < nblk);
-    const uint32_t bits = (uint32_t)__ballot(valid) & 0xFFu;   // lanes 0..7: rows 8w..8w+7
-    if (lane == 0) *((LDS_AS uint8_t*)(LDS_AS void*)vmask + s * 4 + w) = (uint8_t)bits;
+    if (lane < 8) vbias[s][8 * w + lane] = valid ? 0.f : kNegInf;   // lanes 0..7: rows 8w..8w+7
+  };
+  // biases of keys 16kt + 4g + r of stage s
+  auto load_bias = [&](int s, f32x4 (&bias)[KT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) bias[kt] = lds_load<f32x4>((const char*)&vbias[s][0], (16 * kt + 4 * g) * 4);
   };
 
   auto qk_off = [&](int i) __attribute__((always_inline)) {
@@ -240,18 +244,17 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
     bool any;
     bf16x8 s;
   };
-  auto soft_step = [&](auto K, Soft& sm, const f32x4 (&pacc)[2][KT], uint32_t vm) __attribute__((always_inline)) {
+  auto soft_step = [&](auto K, Soft& sm, const f32x4 (&pacc)[2][KT], const f32x4 (&bias)[KT])
+      __attribute__((always_inline)) {
     constexpr int k = decltype(K)::value;
     if constexpr (k == 0) {
-      const uint32_t vmg = vm >> (4 * g);   // validity of keys 4g + (16kt + r)
-      // scaled logits in log2 units; invalid slots masked
+      // scaled logits in log2 units; an invalid slot's bias of -inf masks it
+      // (a valid slot's bias of 0 leaves the product as it is)
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = (pacc[0][kt][r] + pacc[1][kt][r]) * a.scale_log2;
-          sm.x[kt][r] = (vmg >> (16 * kt + r)) & 1u ? v : kNegInf;
-        }
+        for (int r = 0; r < 4; ++r)
+          sm.x[kt][r] = __builtin_fmaf(pacc[0][kt][r] + pacc[1][kt][r], a.scale_log2, bias[kt][r]);
       float c = sm.x[0][0];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
@@ -273,14 +276,13 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
       st.running_max_for_softmax = sm.any ? rmax : st.running_max_for_softmax;
       st.sumexp *= sm.alpha;
     } else if constexpr (k == 3 || k == 4) {
-      // exponentials (a masked slot weighs exactly 0, also before any valid slot)
+      // exponentials: a masked slot weighs exp2(-inf) = 0.  While the running
+      // max is still -inf every score of the head is -inf, so any finite
+      // offset gives the same zeros (and -inf - -inf would be NaN).
       constexpr int kt = k - 3;
-      const float m = st.running_max_for_softmax;
+      const float m = st.running_max_for_softmax == kNegInf ? 0.f : st.running_max_for_softmax;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float xv = sm.x[kt][r];
-        sm.x[kt][r] = xv == kNegInf ? 0.f : __builtin_amdgcn_exp2f(xv - m);
-      }
+      for (int r = 0; r < 4; ++r) sm.x[kt][r] = __builtin_amdgcn_exp2f(sm.x[kt][r] - m);
     } else if constexpr (k == 5) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
@@ -320,9 +322,10 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
     barrier_no_vm_drain();
     f32x4 pacc[2][KT];
     qk(st0, pacc, [&](auto) {});
-    const uint32_t vm = lds_load<uint32_t>((const char*)vmask, 0);
+    f32x4 bias[KT];
+    load_bias(0, bias);
     Soft sm;
-    static_for<0, NSOFT>([&](auto K) __attribute__((always_inline)) { soft_step(K, sm, pacc, vm); });
+    static_for<0, NSOFT>([&](auto K) __attribute__((always_inline)) { soft_step(K, sm, pacc, bias); });
     publish(sm, 0);
   }
 
@@ -360,14 +363,13 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
 
     bf16x8 sop[NW];
     float alph[NW];
-    uint32_t vm = 0;
+    f32x4 bias[KT];
     auto consume_reads = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int ht = 0; ht < NW; ++ht) {
         sop[ht] = lds_load<bf16x8>(xss[p], (ht * 64 + lane) * 16);
         alph[ht] = lds_load<float>((const char*)xas[p], (ht * 16 + n) * 4);
       }
-      vm = lds_load<uint32_t>((const char*)vmask, ((s + 1) & 3) * 4);
     };
     const char* const tile = stages[s];
     i16x4 va[PFV], vb[PFV];
@@ -381,6 +383,8 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
       qk(stages[(s + 1) & 3], pacc, [&](auto I) __attribute__((always_inline)) {
         constexpr int q = decltype(I)::value;
         if constexpr (q == 0) consume_reads();
+        // score biases of block i+1, shortly before its softmax needs them
+        if constexpr (q == NQ - 4) load_bias((s + 1) & 3, bias);
         // first V fragments of PV(i), once few K reads remain in flight
         if constexpr (q >= NQ - PF && q < NQ - PF + 2 * PFV && (q - (NQ - PF)) % 2 == 0)
           fetch_v((q - (NQ - PF)) / 2);
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
       st.o[ht * 8 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, sop[ht], st.o[ht * 8 + jj], 0, 0, 0);
       if constexpr (ht == NW - 1 && jj + PFV < 8) fetch_v(jj + PFV);
       if constexpr (c % 4 == 1 && c / 4 < NSOFT) {
-        if (next) soft_step(std::integral_constant<int, c / 4>{}, sm, pacc, vm);
+        if (next) soft_step(std::integral_constant<int, c / 4>{}, sm, pacc, bias);
       }
       dma_at(std::integral_constant<int, NQ + c>{});
       __builtin_amdgcn_sched_barrier(0);
