@@ -20,6 +20,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -116,9 +118,10 @@ __device__ __forceinline__ float wave_sum16x4(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// a in the low half, b in the high half, each rounded to nearest even (one
+// v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 }  // namespace

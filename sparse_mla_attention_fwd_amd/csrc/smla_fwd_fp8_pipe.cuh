@@ -29,8 +29,6 @@
 namespace smla {
 namespace {
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-
 // 16 E4M3 codes -> two bf16 MFMA operands (codes 0..7, 8..15), exact.
 __device__ __forceinline__ void fp8x16_to_bf16(const i32x4 c, bf16x8& lo, bf16x8& hi) {
   union { bf16x2 p[4]; bf16x8 v; } a, b;
