@@ -331,16 +331,20 @@ __device__ __forceinline__ void compute_block(const char* tile, const LaneOffset
   st.running_max = rmax;
   const bool trig = rmax - st.running_max_for_softmax > kRescaleThresLog2;
   if (__ballot(trig) != 0ull) {
-    // exp2(-inf) = 0 on the first block: the zero state stays zero.
-    const float alpha = __builtin_amdgcn_exp2f(st.running_max_for_softmax - rmax);
+    // On the first block (running_max_for_softmax still -inf in every lane,
+    // as every block holds a valid slot) the accumulators and sums are zero
+    // and stay zero: only the max moves.
+    if (st.running_max_for_softmax != kNegInf) {
+      const float alpha = __builtin_amdgcn_exp2f(st.running_max_for_softmax - rmax);
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      // The accumulators live in AGPRs (MFMA C/D); pinning the rescaled values
-      // back there keeps the register allocator from moving all 128 of them to
-      // VGPRs around the loop for this rarely taken branch.
-      st.o[dt] = pin_agpr(pin_agpr(st.o[dt]) * alpha);
+      for (int dt = 0; dt < 32; ++dt) {
+        // The accumulators live in AGPRs (MFMA C/D); pinning the rescaled values
+        // back there keeps the register allocator from moving all 128 of them to
+        // VGPRs around the loop for this rarely taken branch.
+        st.o[dt] = pin_agpr(pin_agpr(st.o[dt]) * alpha);
+      }
+      st.sumexp *= alpha;
     }
-    st.sumexp *= alpha;
     st.running_max_for_softmax = rmax;
   }
   const float m = st.running_max_for_softmax;

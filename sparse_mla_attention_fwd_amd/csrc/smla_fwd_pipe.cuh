@@ -270,9 +270,11 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
       st.running_max = rmax;
       const bool trig = rmax - st.running_max_for_softmax > kRescaleThresLog2;
       sm.any = __ballot(trig) != 0ull;
-      // exp2(-inf) = 0 when nothing was valid before: the zero state stays zero
+      // While a head has seen no valid slot its accumulators and sum are still
+      // zero, so its factor is 1 (not exp2(-inf) = 0): the first block never
+      // takes the rescale branch.
       const float al = __builtin_amdgcn_exp2f(st.running_max_for_softmax - rmax);
-      sm.alpha = sm.any && rmax != kNegInf ? al : 1.0f;
+      sm.alpha = sm.any && st.running_max_for_softmax != kNegInf ? al : 1.0f;
       st.running_max_for_softmax = sm.any ? rmax : st.running_max_for_softmax;
       st.sumexp *= sm.alpha;
     } else if constexpr (k == 3 || k == 4) {
