@@ -237,6 +237,25 @@ def test_fp8_random_cases(dev, h_q, num_splits):
     check(out, lse, ro, rl, f"fp8 h{h_q} splits={num_splits}")
 
 
+@pytest.mark.parametrize("h_q", [64, 128])
+@pytest.mark.parametrize("topk,num_splits", [(1100, 1), (2048, 2)])
+def test_fp8_long_split_cases(dev, h_q, topk, num_splits):
+    """The pipelined fp8 kernel over many blocks: whole blocks masked before
+    the first valid slot (the running max is still -inf there), a single
+    valid slot at the end, trailing blocks skipped, no valid slot."""
+    x = workloads.make_random(s_q=6, h_q=h_q, topk=topk, s_kv=5000, seed=topk + h_q + 7 * num_splits,
+                              kv_format="fp8", invalid_frac=0.2, dup_frac=0.05, q_mult=2.0)
+    idx = x["indices"]
+    idx[1, :] = -1                           # no valid slot
+    idx[2, :700] = -1                        # leading blocks without a valid slot
+    idx[3, :topk - 1] = 10 ** 6              # only the last slot valid
+    idx[4, 40:] = -1                         # trailing blocks skipped
+    out, lse = run_gpu(dev, x, num_splits=num_splits)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"fp8 long h{h_q} topk={topk} splits={num_splits}")
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
 def test_fp8_single_row_matches_dequant(dev):
     """All slots on one row: out is that row's V = code * scale.  The codes are
     used exactly and the scale enters through the bf16 S operand, so each
