@@ -167,7 +167,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(tokens shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+              "(query tokens are independent, so they would shard across GPUs with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import torch
