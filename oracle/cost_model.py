@@ -8,9 +8,9 @@ cycles are the bytes of Q and O (h_q * d * 2 * 2) plus the gathered KV
 (topk * d * 2) divided by the per-core, per-cycle share of the L2 bandwidth.
 
 The page prints this model's output for its own chip; the golden fixture
-``tests/golden/ascend_cost_model.txt`` holds that printed table.  The same
-model, with MI355X constants, is how the repository's design notes assess
-which unit bounds the kernel.
+``tests/golden/ascend_cost_model.txt`` holds that printed table.  With
+MI355X constants the same model tells which unit, the matrix cores or the
+memory system, bounds the kernel.
 """
 from __future__ import annotations
 
