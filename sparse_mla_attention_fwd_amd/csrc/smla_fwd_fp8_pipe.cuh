@@ -430,8 +430,15 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
     }
 
     if (__ballot(alph[0] != 1.0f || alph[1] != 1.0f || alph[2] != 1.0f || alph[3] != 1.0f) != 0ull) {
-#pragma unroll
-      for (int t = 0; t < 32; ++t) st.o[t] = pin_agpr(pin_agpr(st.o[t]) * alph[t / 8]);
+      static_for<0, NW>([&](auto H) __attribute__((always_inline)) {
+        constexpr int ht = decltype(H)::value;
+        if (__ballot(alph[ht] != 1.0f) != 0ull) {   // only the head tiles whose owner rescaled
+          static_for<0, 8>([&](auto J) __attribute__((always_inline)) {
+            constexpr int t = ht * 8 + decltype(J)::value;
+            st.o[t] = pin_agpr(pin_agpr(st.o[t]) * alph[ht]);
+          });
+        }
+      });
     }
 
     // ---- Oᵀ += Vᵀ·Sᵀ for this wave's group: MFMA c uses V fragment c/4 and
