@@ -97,12 +97,12 @@ def test_fp4_every_code_and_nibble_order(dev):
     assert np.array_equal(out, np.broadcast_to(want[:, None, :], out.shape))
 
 
-def test_decode_fp4_full_size_sampled(dev):
+def test_decode_fp4_full_size_all_tokens(dev):
     """The fp4 decode workload (128 sequences, 16384 rows each, h_q 64,
-    topk 2048), in the launch configuration bench.py times, on sampled
-    tokens."""
+    topk 2048), in the launch configuration bench.py times, every token
+    compared with the oracle."""
+    from test_parity_gpu import check_whole_config
     x = workloads.make_inputs("decode_fp4")
     out, lse = run_fp4(dev, x, num_splits=x["workload"].num_splits)
-    tokens = np.array([0, 1, 63, 64, 126, 127])
-    ro, rl = oracle_fp4(x, tokens)
-    check(out[tokens], lse[tokens], ro, rl, "decode_fp4 sampled")
+    ro, rl = oracle_fp4(x)
+    check_whole_config(out, lse, ro, rl, "decode_fp4 all tokens")

@@ -130,13 +130,16 @@ def test_paged_one_row_is_bit_exact(dev):
     assert np.abs(lse[0] - (xr + math.log(k))).max() < 1e-4
 
 
-def test_decode_paged_full_size_sampled(dev):
+def test_decode_paged_full_size_all_tokens(dev):
     """The paged decode workload (64 sequences, pages of 64 rows dealt in a
     random order, h_q 128, topk 512, 4 splits), in the launch configuration
-    bench.py times, checked on sampled tokens."""
+    bench.py times, every token compared with the oracle (run on chunks of
+    tokens so that only the pages of a chunk are expanded at a time)."""
+    from test_parity_gpu import check_whole_config
     x = workloads.make_inputs("decode_paged")
     w = x["workload"]
     out, lse = run_paged(dev, x, num_splits=w.num_splits)
-    tokens = [0, 17, 63]
-    ro, rl = oracle_paged(x, tokens)
-    check(out[tokens], lse[tokens], ro, rl, "decode_paged sampled")
+    parts = [oracle_paged(x, list(range(t0, min(w.s_q, t0 + 8)))) for t0 in range(0, w.s_q, 8)]
+    ro = np.concatenate([p[0] for p in parts])
+    rl = np.concatenate([p[1] for p in parts])
+    check_whole_config(out, lse, ro, rl, "decode_paged all tokens")

@@ -205,25 +205,33 @@ def test_strided_views(dev):
     assert torch.all(lb[:, :8] == 7) and torch.all(lb[:, 24:] == 7)
 
 
-# ---- full-size workloads: the launch the benchmark times, checked on sampled tokens
+# ---- full-size workloads: the launch the benchmark times, every token compared
 
 
-def _sampled(dev, x, tokens, **kw):
+def check_whole_config(out, lse, ro, rl, what):
+    """The parity bar over the whole configuration (tolerance from max|out|
+    over every token), plus the worst per-token ratio err_t / max|out_t| as a
+    diagnostic."""
+    rel, lerr = check(out, lse, ro, rl, what)
+    den = np.maximum(np.abs(ro).reshape(ro.shape[0], -1).max(axis=1), 1e-30)
+    per = np.abs(out - ro).reshape(ro.shape[0], -1).max(axis=1) / den
+    worst = int(np.argmax(per))
+    _say(f"  {what}: {ro.shape[0]} tokens, worst token {worst} at {per[worst]:.3e} of its own max|out|")
+    return rel, lerr
+
+
+def _whole(dev, x, **kw):
     out, lse = run_gpu(dev, x, **kw)
-    ro, rl = oracle_tokens(x, tokens)
-    return check(out[tokens], lse[tokens], ro, rl, f"{x['workload'].name} sampled")
+    ro, rl = oracle_tokens(x)
+    return check_whole_config(out, lse, ro, rl, f"{x['workload'].name} all tokens")
 
 
-def test_prefill_full_size_sampled(dev):
-    x = workloads.make_inputs("prefill")
-    tokens = np.array([0, 1, 777, 2048, 4094, 4095])
-    _sampled(dev, x, tokens)
+def test_prefill_full_size_all_tokens(dev):
+    _whole(dev, workloads.make_inputs("prefill"))
 
 
-def test_causal_full_size_sampled(dev):
-    x = workloads.make_inputs("causal")
-    tokens = np.array([0, 1, 2, 31, 32, 33, 63, 64, 65, 2046, 2047, 2048, 5000, 8191])
-    _sampled(dev, x, tokens)
+def test_causal_full_size_all_tokens(dev):
+    _whole(dev, workloads.make_inputs("causal"))
 
 
 @pytest.mark.parametrize("h_q", [16, 64])
@@ -274,14 +282,44 @@ def test_fp8_single_row_matches_dequant(dev):
         assert np.abs(lse[t] - (xr + math.log(64))).max() < 1e-4
 
 
-def test_decode_fp8_full_size_sampled(dev):
+def test_decode_fp8_full_size_all_tokens(dev):
     x = workloads.make_inputs("decode_fp8")
-    _sampled(dev, x, np.array([0, 1, 63, 64, 126, 127]))
+    _whole(dev, x, num_splits=x["workload"].num_splits)
 
 
 def test_decode_full_size_all_tokens(dev):
     x = workloads.make_inputs("decode")
-    _sampled(dev, x, np.arange(64), num_splits=4)
+    _whole(dev, x, num_splits=x["workload"].num_splits)
+
+
+# every finite E4M3 code (254 of 256: 0x7F and 0xFF are NaN), walked along the
+# V columns of 16 rows, each row a different rotation of the list
+FP8_FINITE_CODES = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+
+
+@pytest.mark.parametrize("h_q,num_splits", [(16, 1), (32, 1), (64, 1), (64, 2), (128, 2)])
+def test_fp8_every_code_bit_exact(dev, h_q, num_splits):
+    """Unit scales and every slot of token t on row t: all logits are equal,
+    S = 1, the product sums k copies of the code value exactly in fp32, and
+    out/l rounds back to the code value.  So out must equal the E4M3 value of
+    each column's code exactly, for all 254 finite codes (subnormals and both
+    zeros included; the sign of a zero is not pinned, the accumulator starts at
+    +0).  Pins the in-kernel conversion of every code in both the pipelined
+    (64 heads per workgroup) and the cooperative (16, 32 heads) kernels."""
+    n = 16
+    x = workloads.make_random(s_q=n, h_q=h_q, topk=64, s_kv=n, seed=h_q + num_splits, kv_format="fp8")
+    cols = np.arange(576)
+    codes = np.stack([FP8_FINITE_CODES[(cols * 3 + 17 * r) % FP8_FINITE_CODES.size] for r in range(n)])
+    assert all(np.unique(codes[r, :512]).size == FP8_FINITE_CODES.size for r in range(n))
+    x["kv_codes"] = torch.from_numpy(codes.astype(np.uint8))
+    x["kv_scales"] = torch.ones((n, 5), dtype=torch.float32)
+    x["indices"] = torch.arange(n, dtype=torch.int32)[:, None].repeat(1, 64)
+    out, lse = run_gpu(dev, x, num_splits=num_splits)
+    want = dequant_fp8_rows(codes, np.ones((n, 5), dtype=np.float32))[:, :512]
+    assert np.array_equal(out, np.broadcast_to(want[:, None, :], out.shape))
+    for t in range(n):
+        xr = (workloads.to_f64(x["q"][t]) @ dequant_fp8_rows(codes[t:t + 1], np.ones((1, 5)))[0]) * x["sm_scale"]
+        assert np.abs(lse[t] - (xr + math.log(64))).max() < 1e-3
 
 
 # ---- long splits (>= 1024 slots, 64 heads per workgroup): the pipelined kernel
@@ -390,3 +428,26 @@ def test_tuned_plan_is_a_valid_plan_and_matches_the_oracle(dev):
     out, lse = run_gpu(dev, x, num_splits=ns, b_topk=bt)
     ro, rl = oracle_tokens(x)
     check(out, lse, ro, rl, f"tuned ns={ns} B{bt}")
+
+
+def test_binding_rejects_host_rows_and_bad_outputs_before_launch(dev):
+    """Device q with host KV (the default of pack_fp8_kv), a float64 lse or an
+    fp32 out: the binding raises before the library sees a pointer, and a
+    correct call afterwards still runs (nothing was enqueued)."""
+    device, smla = dev
+    x = workloads.make_random(s_q=2, h_q=16, topk=40, s_kv=100, seed=3, kv_format="fp8")
+    q, idx = x["q"].to(device), x["indices"].to(device)
+    host_rows = smla.pack_fp8_kv(x["kv_codes"], x["kv_scales"])
+    with pytest.raises(ValueError, match="device"):
+        smla.sparse_mla_fwd(q, host_rows, idx, x["sm_scale"], kv_format="fp8")
+    rows = host_rows.to(device)
+    with pytest.raises(ValueError):
+        smla.sparse_mla_fwd(q, rows, idx, x["sm_scale"], kv_format="fp8",
+                            lse=torch.empty((2, 16), dtype=torch.float64, device=device))
+    with pytest.raises(ValueError):
+        smla.sparse_mla_fwd(q, rows, idx, x["sm_scale"], kv_format="fp8",
+                            out=torch.empty((2, 16, 512), dtype=torch.float32, device=device))
+    out, lse = smla.sparse_mla_fwd(q, rows, idx, x["sm_scale"], kv_format="fp8")
+    torch.cuda.synchronize()
+    ro, rl = oracle_tokens(x)
+    check(out.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64), ro, rl, "after rejections")

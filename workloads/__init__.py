@@ -144,23 +144,24 @@ def _normal_fp4_groups(rng: np.random.Generator, rows: int, cols: int,
     float32 scale per group (scale = absmax / 6); the code is the nearest E2M1
     value of value / scale, ties to the even mantissa."""
     ng = -(-cols // FP8_GROUP)
-    codes = np.empty((rows, cols), dtype=np.uint8)
-    scales = np.empty((rows, ng), dtype=np.float32)
+    codes = torch.empty((rows, cols), dtype=torch.uint8)
+    scales = torch.empty((rows, ng), dtype=torch.float32)
+    mids = torch.from_numpy(_FP4_MID)
     for r0 in range(0, rows, chunk_rows):
         r1 = min(rows, r0 + chunk_rows)
-        x = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
+        x = torch.from_numpy(rng.standard_normal((r1 - r0, cols), dtype=np.float32))
         for g in range(ng):
             c0, c1 = g * FP8_GROUP, min(cols, (g + 1) * FP8_GROUP)
             xs = x[:, c0:c1]
-            amax = np.abs(xs).max(axis=1)
-            sc = np.where(amax > 0, amax / np.float32(FP4_MAX), np.float32(1.0)).astype(np.float32)
-            a = np.minimum(np.abs(xs / sc[:, None]).astype(np.float64), FP4_MAX)
-            mag = np.searchsorted(_FP4_MID, a, side="left")          # nearest; a tie takes the lower
-            tie_up = (mag < 7) & (a == _FP4_MID[np.minimum(mag, 6)]) & (mag % 2 == 1)
-            mag = (mag + tie_up).astype(np.uint8)                    # ties to the even mantissa
-            codes[r0:r1, c0:c1] = mag | np.where((xs < 0) & (mag > 0), 8, 0).astype(np.uint8)
+            amax = xs.abs().amax(dim=1)
+            sc = torch.where(amax > 0, amax / np.float32(FP4_MAX), torch.ones_like(amax))
+            a = (xs / sc[:, None]).abs().to(torch.float64).clamp_(max=FP4_MAX)
+            mag = torch.bucketize(a, mids, right=False)      # nearest; a tie takes the lower
+            tie_up = (mag < 7) & (a == mids[mag.clamp(max=6)]) & (mag % 2 == 1)
+            mag = (mag + tie_up.to(mag.dtype)).to(torch.uint8)   # ties to the even mantissa
+            codes[r0:r1, c0:c1] = mag | torch.where((xs < 0) & (mag > 0), 8, 0).to(torch.uint8)
             scales[r0:r1, g] = sc
-    return torch.from_numpy(codes), torch.from_numpy(scales)
+    return codes, scales
 
 
 def _indices(rng: np.random.Generator, w: Workload) -> np.ndarray:
