@@ -55,6 +55,16 @@ def test_struct_layouts_match_header(tmp_path, struct, cname):
 
 FAKE = 1 << 20   # 16-byte aligned fake device addresses: never dereferenced on failure paths
 
+# The entry points that enqueue work (smla_fwd, smla_fwd_paged, smla_fwd_tune)
+# are called with the fake addresses only where no GPU is visible: should a
+# check ever regress there, the launch fails for want of a device instead of
+# running a kernel on unmapped addresses.  Rejection itself is checked through
+# the calls that share the same validation and never launch (smla_fwd_plan and
+# the workspace queries); the checks that only the launching calls make
+# (workspace size and alignment) are covered with real device buffers in
+# tests/test_abi_gpu.py.
+NO_GPU = torch.cuda.device_count() == 0
+
 
 def _params(**kw):
     p = _lib.smla_fwd_params()
@@ -94,12 +104,13 @@ def _params(**kw):
 def test_invalid_arguments_are_rejected_on_the_host(field, value, status):
     lib = _lib.load()
     p = _params(**{field: value})
-    # smla_fwd would enqueue work on success; every case here fails validation
-    # first, so no HIP call is made and no GPU is needed.
-    assert lib.smla_fwd(ctypes.byref(p), None) == status
+    ns, bt = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.smla_fwd_plan(ctypes.byref(p), ctypes.byref(ns), ctypes.byref(bt)) == status
     assert _lib.last_error() != ""
     n = ctypes.c_size_t(123)
     assert lib.smla_fwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    if NO_GPU:
+        assert lib.smla_fwd(ctypes.byref(p), None) == status
 
 
 def test_null_params_and_status_strings():
@@ -124,9 +135,10 @@ def test_workspace_required_for_split_plans():
     parts = 4 * 3 * 16
     # fp32 lse per part (256-byte aligned), then the bf16 output of every part
     assert need == parts * 512 * 2 + ((parts * 4 + 255) // 256) * 256
-    assert lib.smla_fwd(ctypes.byref(p), None) == _lib.SMLA_ERR_WORKSPACE
-    p.workspace, p.workspace_bytes = FAKE * 6, need - 1
-    assert lib.smla_fwd(ctypes.byref(p), None) == _lib.SMLA_ERR_WORKSPACE
+    if NO_GPU:
+        assert lib.smla_fwd(ctypes.byref(p), None) == _lib.SMLA_ERR_WORKSPACE
+        p.workspace, p.workspace_bytes = FAKE * 6, need - 1
+        assert lib.smla_fwd(ctypes.byref(p), None) == _lib.SMLA_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("name,splits", [("tiny", None), ("prefill", 1), ("causal", 1), ("decode", 4),
@@ -204,23 +216,29 @@ def test_paged_arguments_are_rejected_on_the_host(field, value, status):
     lib = _lib.load()
     p = _params()
     g = _paged(**{field: value})
-    assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == status
-    assert _lib.last_error() != ""
     n = ctypes.c_size_t(123)
     assert lib.smla_fwd_paged_workspace_size(ctypes.byref(p), ctypes.byref(g), ctypes.byref(n)) == status
+    assert _lib.last_error() != ""
+    if NO_GPU:
+        assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == status
 
 
 def test_paged_workspace_and_null_paged():
     lib = _lib.load()
     p = _params()
-    assert lib.smla_fwd_paged(ctypes.byref(p), None, None) == _lib.SMLA_ERR_INVALID_ARGUMENT
+    n = ctypes.c_size_t(123)
+    assert lib.smla_fwd_paged_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == \
+        _lib.SMLA_ERR_INVALID_ARGUMENT
+    if NO_GPU:
+        assert lib.smla_fwd_paged(ctypes.byref(p), None, None) == _lib.SMLA_ERR_INVALID_ARGUMENT
     g = _paged()
     # translated indices first (s_q * topk int32, 256-byte rounded), then the split region
     p.num_splits = 1
     assert _lib.smla_fwd_paged_workspace_size(p, g) == 4 * 128 * 4
     p.num_splits = 3
     assert _lib.smla_fwd_paged_workspace_size(p, g) == 4 * 128 * 4 + _lib.smla_fwd_workspace_size(p)
-    assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == _lib.SMLA_ERR_WORKSPACE
+    if NO_GPU:
+        assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == _lib.SMLA_ERR_WORKSPACE
     p.s_q = 0
     assert lib.smla_fwd_paged(ctypes.byref(p), ctypes.byref(g), None) == _lib.SMLA_OK
 
@@ -269,7 +287,8 @@ def test_tune_arguments_and_workspace():
     assert lib.smla_fwd_tune(ctypes.byref(p), None, 0, *args) == _lib.SMLA_ERR_INVALID_ARGUMENT
     assert lib.smla_fwd_tune(ctypes.byref(p), None, 10, None, ctypes.byref(bt), None) == \
         _lib.SMLA_ERR_INVALID_ARGUMENT
-    assert lib.smla_fwd_tune(ctypes.byref(p), None, 10, *args) == _lib.SMLA_ERR_WORKSPACE
+    if NO_GPU:
+        assert lib.smla_fwd_tune(ctypes.byref(p), None, 10, *args) == _lib.SMLA_ERR_WORKSPACE
     bad = _params(h_q=24)
     assert lib.smla_fwd_tune(ctypes.byref(bad), None, 10, *args) == _lib.SMLA_ERR_UNSUPPORTED
     # nothing to time: the planner's plan, no HIP call
