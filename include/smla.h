@@ -64,10 +64,13 @@ extern "C" {
 #define SMLA_FP8_NUM_GROUPS 5
 #define SMLA_FP8_ROW_BYTES 640
 
-/* fp4 KV cache (the pages name an FP4 cache for decode beside the FP8 one,
- * section on decoding): OCP MX E2M1 codes (1 sign, 2 exponent, 1 mantissa
- * bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two per byte,
- * with the same five float32 group scales.  A 320-byte row: bytes [0, 288)
+/* fp4 KV cache: page "Ascend Sparse Attention Forward 算法与优化技术简析",
+ * section 讨论 (item "Dequantize bound"), has decode read an FP8 or an FP4 KV
+ * cache and dequantise it to bf16 before the matrix products, and its section
+ * "Decoding KV Cache Layout 优化" keeps each token's data next to its scales.
+ * Neither fixes the 4-bit format; here: OCP MX E2M1 codes (1 sign, 2
+ * exponent, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ * negatives), two per byte, with the same five float32 group scales.  A 320-byte row: bytes [0, 288)
  * hold column 2k in the low nibble and column 2k+1 in the high nibble of byte
  * k, bytes [288, 308) the five scales, bytes [308, 320) padding.
  * Element value = e2m1(code) * scale[column / 128]. */
@@ -191,6 +194,9 @@ smla_status smla_fwd_paged(const smla_fwd_params* p, const smla_paged_kv* paged,
 
 /* ---- Shape-dependent plan selection.
  *
+ * Page "FlashMLA算子Ascend 950移植：从tiling到访存优化全解读", section 6
+ * (后续优化方向, dynamic tiling): the best tile depends on the request's
+ * shape, so prepared tiling configurations are chosen per shape at run time.
  * The planner's choice (num_splits = b_topk = 0) follows measured behaviour
  * on the named workloads; for other shapes a caller can time the candidate
  * plans on its own inputs once and pass the winner explicitly (the library
