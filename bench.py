@@ -5,7 +5,11 @@
 A step is one forward pass over the whole workload (every token, every
 head): one call of the library's entry point, which launches the fused
 kernel (plus the split combine for decode plans).  Inputs are resident in HBM
-before the timed region; K steps run back to back between two device
+before the timed region.  Before every timed step a 512 MiB scratch buffer is
+written (outside the step's events), so that neither the L2 nor the 256 MB
+MALL holds anything of the inputs from the previous step; the step itself is
+bracketed by HIP events on its stream, and the median over the K steps is the
+step time.  The K steps with their flushes run between two device
 synchronisations.  Prints one JSON line.
 
 Default workload: prefill, 4096 query tokens, h_q 64, topk 2048, d_qk 576,
@@ -13,12 +17,17 @@ d_v 512, one shared bf16 KV of 65536 rows, indices uniform without
 replacement per token.
 
 ``roofline``: algorithmic FLOPs of one launch (2·h_q·(d_qk + d_v) per valid
-slot) over the average launch duration, measured with HIP events recorded on
+slot) over the median launch duration, measured with HIP events recorded on
 the stream the kernel runs on, against the MI355X dense bf16 MFMA peak; for
 the decode workloads (HBM-bound) the algorithmic bytes of one launch over the
 same duration against the 8 TB/s HBM peak.
+``binding``: the gathered rows (every valid slot's KV row) per launch over the
+same duration, against the measured random-row gather ceiling of the memory
+system (``profiles/gather_ceiling.json``, from ``bench/micro/gather_ceiling``):
+the roof that actually binds a kernel whose rows come at random from the MALL
+or HBM.
 ``cpu_baseline``: the float64 CPU oracle timed on this host over a bounded
-sample of the same workload's tokens.
+sample of the same workload's tokens, with every BLAS thread and with one.
 """
 from __future__ import annotations
 
@@ -35,6 +44,40 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sparse_mla_attention_fwd_amd", "csrc")
+FLUSH_MIB = 512                  # > 2x the 256 MB MALL, > 60x one XCD's 4 MB L2
+
+
+def gather_ceiling(w):
+    """The measured random-row gather ceiling that applies to a workload:
+    (GB/s, regime name) from profiles/gather_ceiling.json, or (None, None)."""
+    path = os.path.join(ROOT, "profiles", "gather_ceiling.json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        rec = json.load(f)
+    if w.seqs == 1:
+        key = "bf16_mall"            # one shared KV that fits the MALL
+    else:
+        key = {"bf16": "bf16_hbm", "fp8": "fp8_hbm", "fp4": "fp8_hbm"}[w.kv_format]
+    c = rec.get("ceilings", {}).get(key)
+    return (c["gbs"], c["regime"]) if c else (None, None)
+
+
+def cpu_description():
+    """CPU model name and the BLAS library numpy calls."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    from threadpoolctl import threadpool_info
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', 'n/a')})"
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    return model, ", ".join(blas) or "unknown"
 
 
 def kernel_hash() -> str:
@@ -73,6 +116,22 @@ def algorithmic_bytes(w) -> int:
 
 
 def cpu_baseline(x, budget_s: float):
+    """The float64 oracle timed on this host: with every BLAS thread for
+    budget_s seconds of oracle time, then with one thread for a third of that
+    (each on the first tokens of the workload, at least 16)."""
+    from threadpoolctl import threadpool_limits
+    res = _cpu_oracle_rate(x, budget_s)
+    with threadpool_limits(limits=1):
+        one = _cpu_oracle_rate(x, budget_s / 3)
+    model, blas = cpu_description()
+    res["single_thread"] = {"value": one["value"], "unit": one["unit"], "sample": one["sample"]}
+    res["cpu_model"] = model
+    res["blas"] = blas
+    res["logical_cpus"] = os.cpu_count()
+    return res
+
+
+def _cpu_oracle_rate(x, budget_s: float):
     """Time the float64 oracle on the first tokens of the workload until the
     time budget is used (at least 16 tokens)."""
     import numpy as np
@@ -153,12 +212,14 @@ def _cpu_result(w, valid, t_used, done, kind):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--b-topk", type=int, default=0)
     ap.add_argument("--num-splits", type=int, default=-1, help="-1: the workload's own setting")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 skips")
+    ap.add_argument("--flush-mib", type=int, default=FLUSH_MIB,
+                    help="MiB written before every timed step to evict the inputs from L2 and MALL")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -240,39 +301,51 @@ def main():
         step()
         torch.cuda.synchronize()
 
-    # per-launch durations with events on the launch stream
+    # Per-step durations with events on the launch stream.  Before each step a
+    # scratch buffer larger than the MALL is written (outside the events), so
+    # the step finds its inputs in HBM, not in a cache warmed by the last step.
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
-    ms_per_step = wall / args.steps * 1e3
+    launch_ms = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
+    n = len(launch_ms)
+    median_ms = launch_ms[n // 2] if n % 2 else 0.5 * (launch_ms[n // 2 - 1] + launch_ms[n // 2])
+    mean_ms = sum(launch_ms) / n
+    step_s = median_ms / 1e3
 
     flops = w.flops
-    value = flops / (ms_per_step / 1e3) / 1e12
-    achieved = flops / avg_launch_s / 1e12
+    value = flops / step_s / 1e12
     traffic = load_traffic(w.name, flops)
     row_bytes = {"bf16": 1152, "fp8": 640, "fp4": 320}[fmt]
     gathered = w.valid_slots * row_bytes
+    gather_gbs = gathered / step_s / 1e9
 
     if w.seqs > 1:
         # decode: HBM-bound (arithmetic intensity below the MFMA/HBM ridge)
         alg = algorithmic_bytes(w)
-        gbs = alg / avg_launch_s / 1e9
+        gbs = alg / step_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "algorithmic_bytes": alg, "tflops": round(achieved, 2)}
+                    "algorithmic_bytes": alg, "tflops": round(value, 2)}
     else:
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        roofline = {"bound": "mfma", "achieved": round(value, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
                     "traffic": traffic}
+    ceiling, regime = gather_ceiling(w)
+    binding = {"bound": "gather", "achieved": round(gather_gbs, 1), "unit": "GB/s",
+               "ceiling": ceiling, "frac": round(gather_gbs / ceiling, 4) if ceiling else None,
+               "ceiling_regime": regime, "source": "profiles/gather_ceiling.md",
+               "gathered_bytes_per_launch": gathered}
     res = {
         "metric": "sparse MLA fwd TFLOP/s and % bf16 MFMA peak (h_q=64, topk=2048, d_qk=576)",
         "value": round(value, 2),
@@ -280,7 +353,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(median_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -291,9 +364,12 @@ def main():
                    "page_size": w.page_size or None, "hip_graph": bool(args.graph),
                    "b_topk": plan_bt, "parallelism": "single GPU"},
         "roofline": roofline,
-        "gather": {"bytes_per_launch": gathered, "GB/s": round(gathered / avg_launch_s / 1e9, 1),
-                   "frac_of_hbm_peak": round(gathered / avg_launch_s / 1e9 / HBM_PEAK_GBS, 4)},
-        "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+        "binding": binding,
+        "timing": {"statistic": f"median of {n} steps, HIP events on the launch stream",
+                   "median_ms": round(median_ms, 4), "mean_ms": round(mean_ms, 4),
+                   "min_ms": round(launch_ms[0], 4), "max_ms": round(launch_ms[-1], 4),
+                   "flush_mib_before_each_step": args.flush_mib,
+                   "wall_ms_per_step_with_flush": round(wall / args.steps * 1e3, 4)},
     }
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)

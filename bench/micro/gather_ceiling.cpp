@@ -1,20 +1,25 @@
 // Gather ceiling of the memory system: throughput of random-row gathers with
-// the access pattern of the forward kernels (one wave instruction loads eight
-// random rows x one 128-byte line, 16 bytes per lane), measured for the row
-// sizes and table sizes of the sparse MLA workloads.
+// the access patterns of the forward kernels, measured for the row sizes and
+// table sizes of the sparse MLA workloads.
 //
 //   rows of 1152 bytes (bf16 KV) from 64 slices of 37.7 MB (decode: each
-//     workgroup reads rows of one sequence) and from one 75.5 MB table
-//     (prefill: the KV is small enough for the 256 MB MALL)
+//     workgroup reads rows of one sequence), from one 75.5 MB table (prefill:
+//     the KV is small enough for the 256 MB MALL) and from one 2.4 MB table
+//     (small enough for each XCD's 4 MB L2: the load path's own limit)
 //   rows of 640 bytes (packed fp8 KV) from 128 slices of 10.5 MB
 //
-// Variants: direct-to-LDS loads (what the kernels use) with D instructions in
-// flight per wave, 4/8/16 waves per workgroup, one or two workgroups per CU;
-// and plain loads into registers.  Every address lies inside the buffer: row
-// = hash % rows_per_slice, line j < row_bytes / 128.
+// Access shapes of one wave instruction (64 lanes x 16 bytes):
+//   lines:  eight random rows x one 128-byte line (the bf16 kernels' shape);
+//   rows:   64 consecutive 16-byte chunks of the wave's eight rows laid end to
+//           end, i.e. 1 KB of one or two rows (the raw-row shape of the
+//           quantised kernels).
+// Loads: direct-to-LDS (what the kernels use) with D instructions in flight
+// per wave, 4/8/16 waves per workgroup, one or two workgroups per CU; and
+// plain loads into registers.  Every address lies inside the buffer: row =
+// hash % rows_per_slice, byte offset inside the row < row_bytes.
 //
-// Build and run (no arguments): see sparse_mla_attention_fwd_amd/build.py
-// (build_gather_ceiling) -> sparse_mla_attention_fwd_amd/gather_ceiling.
+// Build: python bench/micro/build.py; run ./bench/micro/gather_ceiling (no
+// arguments).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -50,8 +55,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
-// MODE 0: direct-to-LDS 16-byte loads, at most D in flight per wave.
-// MODE 1: 16-byte loads into registers in batches of D.
+// MODE 0: direct-to-LDS 16-byte loads, at most D in flight per wave, lines shape.
+// MODE 1: 16-byte loads into registers in batches of D, lines shape.
+// MODE 2: direct-to-LDS 16-byte loads, at most D in flight per wave, rows shape.
 template <int MODE, int D>
 __global__ void gather_kernel(const char* __restrict__ kv, uint32_t rows_per_slice, uint32_t nslices,
                               int row_bytes, int groups_per_wave, uint32_t* sink) {
@@ -61,7 +67,24 @@ __global__ void gather_kernel(const char* __restrict__ kv, uint32_t rows_per_sli
   const uint32_t slice = blockIdx.x % nslices;
   const char* base = kv + (uint64_t)slice * rows_per_slice * row_bytes;
   uint32_t acc = 0;
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 2) {
+    // the group's eight rows end to end: instruction j covers chunks
+    // 64j .. 64j + 63 of the 8 x row_bytes / 16 chunks
+    const int chunks = row_bytes / 16;
+    int issued = 0;
+    for (int grp = 0; grp < groups_per_wave; ++grp) {
+      for (int j = 0; j < lines; ++j) {
+        const int c = j * 64 + lane;
+        const int r = c / chunks, ch = c - r * chunks;
+        const uint32_t row = mix32((blockIdx.x * 4096u + w * 512u + grp) * 8u + r) % rows_per_slice;
+        __builtin_amdgcn_global_load_lds((const void*)(base + (uint64_t)row * row_bytes + ch * 16),
+                                         (__attribute__((address_space(3))) void*)(lds + ((w * 8 + (issued & 7)) & 63) * 1024),
+                                         16, 0, 0);
+        wait_vmcnt<D>();
+        ++issued;
+      }
+    }
+  } else if constexpr (MODE == 0) {
     int issued = 0;
     for (int grp = 0; grp < groups_per_wave; ++grp) {
       const uint32_t row = mix32((blockIdx.x * 4096u + w * 512u + grp) * 8u + (lane & 7)) % rows_per_slice;
@@ -115,6 +138,7 @@ int main() {
       {1152, 32768, 64, "bf16 rows, 64 slices of 37.7 MB (HBM)"},
       {640, 16384, 128, "fp8 rows, 128 slices of 10.5 MB (HBM)"},
       {1152, 65536, 1, "bf16 rows, one 75.5 MB table (MALL)"},
+      {1152, 2048, 1, "bf16 rows, one 2.4 MB table (L2)"},
   };
   auto run = [&](auto kernel, const Regime& r, int waves, int wgs, int lds_bytes, int gpw, const char* kind, int d) {
     CHECK(hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes));
@@ -133,20 +157,20 @@ int main() {
                 bytes / ms / 1e6);
     std::fflush(stdout);
   };
-  std::printf("| rows | loads | in flight per wave | waves per WG | WGs | LDS KB per WG | GB/s |\n");
+  std::printf("| table | loads, shape | in flight per wave | waves per WG | WGs | LDS KB per WG | GB/s |\n");
   std::printf("|---|---|---|---|---|---|---|\n");
   for (const Regime& r : regimes) {
     for (int waves : {4, 8, 16}) {
       const int gpw = 256 / waves;   // 2048 rows per workgroup
-      run(gather_kernel<0, 8>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS", 8);
-      run(gather_kernel<0, 16>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS", 16);
-      run(gather_kernel<0, 32>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS", 32);
-      run(gather_kernel<0, 48>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS", 48);
-      run(gather_kernel<1, 16>, r, waves, 1024, 100 * 1024, gpw, "registers", 16);
+      run(gather_kernel<0, 8>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, lines", 8);
+      run(gather_kernel<0, 32>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, lines", 32);
+      run(gather_kernel<2, 8>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, rows", 8);
+      run(gather_kernel<2, 32>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, rows", 32);
+      run(gather_kernel<1, 16>, r, waves, 1024, 100 * 1024, gpw, "registers, lines", 16);
     }
     // two workgroups per CU (64 KB of LDS each)
-    run(gather_kernel<0, 32>, r, 4, 2048, 64 * 1024, 64, "direct-to-LDS", 32);
-    run(gather_kernel<0, 32>, r, 8, 2048, 64 * 1024, 32, "direct-to-LDS", 32);
+    run(gather_kernel<0, 32>, r, 4, 2048, 64 * 1024, 64, "direct-to-LDS, lines", 32);
+    run(gather_kernel<2, 32>, r, 4, 2048, 64 * 1024, 64, "direct-to-LDS, rows", 32);
   }
   CHECK(hipFree(kv));
   CHECK(hipFree(sink));

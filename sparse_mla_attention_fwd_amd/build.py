@@ -67,35 +67,5 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-GATHER_CEILING = os.path.join(HERE, "gather_ceiling")
-ISSUE_PROBE = os.path.join(HERE, "issue_probe")
-
-
-def _build_program(src: str, exe: str, verbose: bool) -> str:
-    cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", "-x", "hip", os.path.join(CSRC, src), "-o", exe + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
-    os.replace(exe + ".tmp", exe)
-    return exe
-
-
-def build_gather_ceiling(verbose: bool = False) -> str:
-    """Compile the gather-ceiling measurement program (csrc/gather_ceiling.cpp);
-    returns the path of the executable."""
-    return _build_program("gather_ceiling.cpp", GATHER_CEILING, verbose)
-
-
-def build_issue_probe(verbose: bool = False) -> str:
-    """Compile the MFMA issue-rate measurement program (csrc/issue_probe.cpp);
-    returns the path of the executable."""
-    return _build_program("issue_probe.cpp", ISSUE_PROBE, verbose)
-
-
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
-    print(build_gather_ceiling(verbose="-v" in sys.argv))
-    print(build_issue_probe(verbose="-v" in sys.argv))

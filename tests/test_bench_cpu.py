@@ -47,3 +47,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name,key", [("prefill", "bf16_mall"), ("causal", "bf16_mall"),
+                                      ("decode", "bf16_hbm"), ("decode_paged", "bf16_hbm"),
+                                      ("decode_fp8", "fp8_hbm"), ("decode_fp4", "fp8_hbm")])
+def test_gather_ceiling_regime_of_each_workload(name, key):
+    """A shared KV small enough for the MALL is held against the MALL ceiling,
+    per-sequence caches against the HBM ceiling of their row size."""
+    rec = json.load(open(os.path.join(ROOT, "profiles", "gather_ceiling.json")))
+    gbs, regime = bench.gather_ceiling(workloads.WORKLOADS[name])
+    assert gbs == rec["ceilings"][key]["gbs"] and regime == rec["ceilings"][key]["regime"]
+
+
+def test_cpu_description_names_the_blas():
+    model, blas = bench.cpu_description()
+    assert model and blas and blas != "unknown"
