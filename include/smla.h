@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 4
+#define SMLA_ABI_VERSION 5
 
 /* The MLA shapes the kernels are built for: the query/key width d_qk is the
  * 512-wide latent plus the 64-wide rotary part, and V is the first 512 KV
@@ -152,6 +152,28 @@ smla_status smla_fwd_workspace_size(const smla_fwd_params* p, size_t* bytes);
 
 /* Enqueue the forward pass: writes out and lse.  Asynchronous on `stream`. */
 smla_status smla_fwd(const smla_fwd_params* p, void* stream);
+
+/* ---- Forward pass without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).
+ *
+ * smla_fwd with the split partials kept in a scratch array the library holds
+ * in each device's memory (SMLA_STATIC_SCRATCH_BYTES, resident on a device
+ * from the first call there until the process ends) instead of
+ * p->workspace, which is ignored.  The call allocates nothing: no hipMalloc,
+ * no hipFree.  A plan whose split partials need more than the scratch holds
+ * (smla_fwd_workspace_size > SMLA_STATIC_SCRATCH_BYTES) returns
+ * SMLA_ERR_WORKSPACE and enqueues nothing; so does a device the library
+ * cannot reach (SMLA_ERR_HIP).  The scratch of a device belongs to the
+ * device of `stream` (the current device for the NULL stream).
+ *
+ * Every call on one device shares that device's scratch.  Calls ordered on
+ * one stream are safe; calls that may overlap in time on one device (other
+ * streams, other host threads) race on it and give wrong results.  Each part
+ * writes all of its partial results before the merge reads them, so nothing
+ * from an earlier call is ever read. */
+#define SMLA_STATIC_SCRATCH_BYTES (64u << 20)
+smla_status smla_fwd_static_scratch(const smla_fwd_params* p, void* stream);
 
 /* ---- Paged KV cache.
  *

@@ -21,11 +21,11 @@ import torch
 from . import _lib
 from ._lib import (D_QK, D_V, FP4_ROW_BYTES, FP8_ROW_BYTES, SMLA_KV_BF16, SMLA_KV_FP4_E2M1,  # noqa: F401
                    SMLA_KV_FP8_E4M3, SmlaError, make_paged, make_params, smla_fwd, smla_fwd_paged,
-                   smla_fwd_paged_workspace_size, smla_fwd_plan, smla_fwd_tune,
+                   smla_fwd_paged_workspace_size, smla_fwd_plan, smla_fwd_static_scratch, smla_fwd_tune,
                    smla_fwd_tune_workspace_size, smla_fwd_workspace_size, smla_pack_fp4_kv_host,
                    smla_pack_fp8_kv_host)
 
-__all__ = ["sparse_mla_fwd", "pack_fp8_kv", "pack_fp4_kv", "smla_fwd", "smla_fwd_plan",
+__all__ = ["sparse_mla_fwd", "pack_fp8_kv", "pack_fp4_kv", "smla_fwd", "smla_fwd_static_scratch", "smla_fwd_plan",
            "smla_fwd_workspace_size", "smla_fwd_paged", "smla_fwd_paged_workspace_size",
            "smla_fwd_tune", "smla_fwd_tune_workspace_size", "tune_plan", "smla_pack_fp8_kv_host",
            "smla_pack_fp4_kv_host", "SmlaError"]

@@ -32,10 +32,12 @@ MAX_SLOTS_PER_SPLIT = 2048
 MAX_SLOTS_PER_SPLIT_FP8 = 1536
 
 # Every symbol include/smla.h declares.
-EXPORTS = ("smla_fwd_plan", "smla_fwd_workspace_size", "smla_fwd", "smla_fwd_paged_workspace_size",
+EXPORTS = ("smla_fwd_plan", "smla_fwd_workspace_size", "smla_fwd", "smla_fwd_static_scratch",
+           "smla_fwd_paged_workspace_size",
            "smla_fwd_paged", "smla_fwd_tune_workspace_size", "smla_fwd_tune", "smla_pack_fp8_kv_host",
            "smla_pack_fp4_kv_host", "smla_status_string", "smla_last_error", "smla_abi_version")
-ABI_VERSION = 4
+ABI_VERSION = 5
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class smla_fwd_params(ctypes.Structure):
@@ -85,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.smla_fwd_workspace_size.restype = ctypes.c_int
     lib.smla_fwd.argtypes = [P, ctypes.c_void_p]
     lib.smla_fwd.restype = ctypes.c_int
+    lib.smla_fwd_static_scratch.argtypes = [P, ctypes.c_void_p]
+    lib.smla_fwd_static_scratch.restype = ctypes.c_int
     G = ctypes.POINTER(smla_paged_kv)
     lib.smla_fwd_paged_workspace_size.argtypes = [P, G, ctypes.POINTER(ctypes.c_size_t)]
     lib.smla_fwd_paged_workspace_size.restype = ctypes.c_int
@@ -140,6 +144,14 @@ def smla_fwd(params: smla_fwd_params, stream: int | None = None):
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
     _check(load().smla_fwd(ctypes.byref(params), ctypes.c_void_p(stream)))
+
+
+def smla_fwd_static_scratch(params: smla_fwd_params, stream: int | None = None):
+    """smla_fwd with the split partials in the library's per-device static
+    scratch (no workspace, no allocation)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    _check(load().smla_fwd_static_scratch(ctypes.byref(params), ctypes.c_void_p(stream)))
 
 
 def smla_fwd_paged_workspace_size(params: smla_fwd_params, paged: smla_paged_kv) -> int:

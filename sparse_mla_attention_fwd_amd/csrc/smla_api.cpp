@@ -1,6 +1,7 @@
 // C-ABI layer: argument validation, planning, workspace sizing and launch.
-// Declared in include/smla.h.  Everything here runs on the host; nothing is
-// enqueued unless every check passes.
+// Declared in include/smla.h.  Everything here runs on the host (the one
+// device object is the static split scratch below); nothing is enqueued
+// unless every check passes.
 #include "smla.h"
 
 #include <hip/hip_runtime.h>
@@ -9,8 +10,16 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "smla_internal.h"
+
+// Split-partial scratch of smla_fwd_static_scratch: one array per device (a
+// __device__ object exists once in every device's memory).  In host code the
+// name stands for a host-side shadow, not a device address: the device
+// address is looked up per device with hipGetSymbolAddress and only that
+// pointer is handed to kernels.
+static __device__ __align__(256) char scratch[SMLA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -246,6 +255,36 @@ size_t translated_bytes(const smla_fwd_params* p) {
   return ((size_t)p->s_q * (size_t)p->topk * sizeof(int32_t) + 255) & ~size_t(255);
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream`, looked up once
+// per device with that device current.
+smla_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SMLA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(SMLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(SMLA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr)
+      return fail(SMLA_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SMLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +321,25 @@ smla_status smla_fwd(const smla_fwd_params* p, void* stream) {
   }
   return launch_plan(p, pl, p->indices, p->indices_stride_token, static_cast<char*>(p->workspace),
                      static_cast<hipStream_t>(stream));
+}
+
+smla_status smla_fwd_static_scratch(const smla_fwd_params* p, void* stream) {
+  Plan pl;
+  const smla_status s = check_and_plan(p, &pl);
+  if (s != SMLA_OK) return s;
+  if (p->s_q == 0) return SMLA_OK;
+  if (pl.workspace_bytes > SMLA_STATIC_SCRATCH_BYTES)
+    return fail(SMLA_ERR_WORKSPACE,
+                "the plan's split partials need %zu bytes, more than the %u-byte static scratch "
+                "(fewer splits or tokens per call fit)", pl.workspace_bytes,
+                (unsigned)SMLA_STATIC_SCRATCH_BYTES);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (pl.workspace_bytes) {
+    const smla_status e = scratch_address(st, &ws);
+    if (e != SMLA_OK) return e;
+  }
+  return launch_plan(p, pl, p->indices, p->indices_stride_token, static_cast<char*>(ws), st);
 }
 
 smla_status smla_fwd_paged_workspace_size(const smla_fwd_params* p, const smla_paged_kv* pg,

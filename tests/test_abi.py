@@ -295,3 +295,20 @@ def test_tune_arguments_and_workspace():
     empty = _params(s_q=0, q=0, kv=0, indices=0, out=0, lse=0)
     assert lib.smla_fwd_tune(ctypes.byref(empty), None, 10, *args) == _lib.SMLA_OK
     assert (ns.value, bt.value) == _lib.smla_fwd_plan(empty)
+
+
+def test_static_scratch_size_and_oversized_plans():
+    """The header's scratch size is the binding's; a plan whose split partials
+    exceed it is refused before anything is enqueued."""
+    text = open(HEADER).read()
+    m = re.search(r"#define SMLA_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.STATIC_SCRATCH_BYTES
+    lib = _lib.load()
+    p = _params(s_q=256, h_q=128, topk=2048, indices_stride_token=2048, num_splits=16,
+                q_stride_token=128 * 576, out_stride_token=128 * 512, lse_stride_token=128)
+    assert _lib.smla_fwd_workspace_size(p) > _lib.STATIC_SCRATCH_BYTES
+    if NO_GPU:
+        assert lib.smla_fwd_static_scratch(ctypes.byref(p), None) == _lib.SMLA_ERR_WORKSPACE
+        assert "static scratch" in _lib.last_error()
+        bad = _params(h_q=24)
+        assert lib.smla_fwd_static_scratch(ctypes.byref(bad), None) == _lib.SMLA_ERR_UNSUPPORTED
