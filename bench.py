@@ -217,6 +217,8 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--b-topk", type=int, default=0)
     ap.add_argument("--num-splits", type=int, default=-1, help="-1: the workload's own setting")
+    ap.add_argument("--schedule", choices=["auto", "grid", "persistent"], default="auto",
+                    help="work schedule: the planner's choice, one workgroup per token, or persistent")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time; 0 skips")
     ap.add_argument("--flush-mib", type=int, default=FLUSH_MIB,
                     help="MiB written before every timed step to evict the inputs from L2 and MALL")
@@ -266,8 +268,12 @@ def main():
     p = smla.make_params(q, kv, idx, x["sm_scale"], out, lse,
                          kv_format={"bf16": smla.SMLA_KV_BF16, "fp8": smla.SMLA_KV_FP8_E4M3,
                                     "fp4": smla.SMLA_KV_FP4_E2M1}[fmt],
-                         num_splits=ns, b_topk=args.b_topk)
+                         num_splits=ns, b_topk=args.b_topk,
+                         schedule={"auto": smla.SMLA_SCHEDULE_AUTO, "grid": smla.SMLA_SCHEDULE_GRID,
+                                   "persistent": smla.SMLA_SCHEDULE_PERSISTENT}[args.schedule])
     plan_splits, plan_bt = smla.smla_fwd_plan(p)
+    plan_schedule = {smla.SMLA_SCHEDULE_GRID: "grid",
+                     smla.SMLA_SCHEDULE_PERSISTENT: "persistent"}[smla.smla_fwd_schedule(p)]
     if w.page_size:
         bt = x["block_table"].to(dev)
         paged = smla.make_paged(bt, w.page_size)
@@ -362,7 +368,7 @@ def main():
         "config": {"workload": w.name, "s_q": w.s_q, "h_q": w.h_q, "topk": w.topk, "s_kv": w.s_kv,
                    "d_qk": 576, "d_v": 512, "kv_format": fmt, "num_splits": plan_splits,
                    "page_size": w.page_size or None, "hip_graph": bool(args.graph),
-                   "b_topk": plan_bt, "parallelism": "single GPU"},
+                   "b_topk": plan_bt, "schedule": plan_schedule, "parallelism": "single GPU"},
         "roofline": roofline,
         "binding": binding,
         "timing": {"statistic": f"median of {n} steps, HIP events on the launch stream",

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 5
+#define SMLA_ABI_VERSION 6
 
 /* The MLA shapes the kernels are built for: the query/key width d_qk is the
  * 512-wide latent plus the 64-wide rotary part, and V is the first 512 KV
@@ -88,6 +88,12 @@ typedef enum smla_status {
   SMLA_ERR_WORKSPACE = 3,        /* workspace missing or too small */
   SMLA_ERR_HIP = 4               /* a HIP runtime call failed */
 } smla_status;
+
+typedef enum smla_schedule {
+  SMLA_SCHEDULE_AUTO = 0,
+  SMLA_SCHEDULE_GRID = 1,
+  SMLA_SCHEDULE_PERSISTENT = 2
+} smla_schedule;
 
 typedef enum smla_kv_format {
   SMLA_KV_BF16 = 0,     /* kv: bf16 [s_kv, 576], kv_stride_row in elements */
@@ -134,20 +140,47 @@ typedef struct smla_fwd_params {
   int32_t num_splits;
   int32_t b_topk;
 
-  /* Device scratch for split partial results, needed when the plan has more
-   * than one split; size from smla_fwd_workspace_size (fp32 lse and bf16
-   * normalised output of every part).  Caller-owned; it may be reused by later
-   * calls on the same stream. */
+  /* Work schedule (page "Flash Attention Infer算子性能优化", section
+   * 优化多核负载均衡: with causal or sparse masks tokens carry different
+   * numbers of valid blocks, so tokens are dealt to the cores by valid-block
+   * weight, not by count).
+   *   schedule: SMLA_SCHEDULE_AUTO (0) lets the planner choose (the grid: on
+   *             the measured workloads the hardware's own dispatch of one
+   *             workgroup per token balances as well, see the design notes);
+   *             SMLA_SCHEDULE_GRID (1): one workgroup per (token, split, group
+   *             of 64 heads);
+   *             SMLA_SCHEDULE_PERSISTENT (2): a fixed number of workgroups,
+   *             each on a contiguous run of tokens of about equal weight
+   *             (blocks up to the token's last valid slot, plus the cost of a
+   *             token switch), with the pipeline running through token
+   *             boundaries.  Built for bf16 KV within a 4 GB byte window,
+   *             h_q = 64, one split and topk >= 1024; SMLA_ERR_UNSUPPORTED
+   *             otherwise.
+   *   persistent_workgroups: workgroups of the persistent schedule; 0 = one
+   *             per compute unit of the device. */
+  int32_t schedule;
+  int32_t persistent_workgroups;
+
+  /* Device scratch, needed when the plan has more than one split (fp32 lse
+   * and bf16 normalised output of every part) or runs one split of the
+   * pipelined 64-head kernel in a 4 GB byte window (int32 block count of
+   * every token, computed ahead); size from smla_fwd_workspace_size.
+   * Caller-owned; it may be reused by later calls on the same stream. */
   void* workspace;
   size_t workspace_bytes;
 } smla_fwd_params;
 
 /* The plan the library would run for these parameters (argument checks
- * included): number of splits and block size. */
+ * included): number of splits and block size.  (Whether the persistent
+ * schedule runs: smla_fwd_schedule.) */
 smla_status smla_fwd_plan(const smla_fwd_params* p, int32_t* num_splits, int32_t* b_topk);
 
+/* The schedule the library would run for these parameters: SMLA_SCHEDULE_GRID
+ * or SMLA_SCHEDULE_PERSISTENT. */
+smla_status smla_fwd_schedule(const smla_fwd_params* p, int32_t* schedule);
+
 /* Bytes of device workspace smla_fwd needs for these parameters (0 when the
- * plan has a single split). */
+ * plan needs none). */
 smla_status smla_fwd_workspace_size(const smla_fwd_params* p, size_t* bytes);
 
 /* Enqueue the forward pass: writes out and lse.  Asynchronous on `stream`. */

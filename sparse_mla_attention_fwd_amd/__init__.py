@@ -20,12 +20,14 @@ import torch
 
 from . import _lib
 from ._lib import (D_QK, D_V, FP4_ROW_BYTES, FP8_ROW_BYTES, SMLA_KV_BF16, SMLA_KV_FP4_E2M1,  # noqa: F401
-                   SMLA_KV_FP8_E4M3, SmlaError, make_paged, make_params, smla_fwd, smla_fwd_paged,
-                   smla_fwd_paged_workspace_size, smla_fwd_plan, smla_fwd_static_scratch, smla_fwd_tune,
+                   SMLA_KV_FP8_E4M3, SMLA_SCHEDULE_AUTO, SMLA_SCHEDULE_GRID, SMLA_SCHEDULE_PERSISTENT, SmlaError, make_paged, make_params, smla_fwd, smla_fwd_paged,
+                   smla_fwd_paged_workspace_size, smla_fwd_plan, smla_fwd_schedule, smla_fwd_static_scratch,
+                   smla_fwd_tune,
                    smla_fwd_tune_workspace_size, smla_fwd_workspace_size, smla_pack_fp4_kv_host,
                    smla_pack_fp8_kv_host)
 
 __all__ = ["sparse_mla_fwd", "pack_fp8_kv", "pack_fp4_kv", "smla_fwd", "smla_fwd_static_scratch", "smla_fwd_plan",
+           "smla_fwd_schedule",
            "smla_fwd_workspace_size", "smla_fwd_paged", "smla_fwd_paged_workspace_size",
            "smla_fwd_tune", "smla_fwd_tune_workspace_size", "tune_plan", "smla_pack_fp8_kv_host",
            "smla_pack_fp4_kv_host", "SmlaError"]
@@ -116,7 +118,8 @@ def tune_plan(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale
 
 def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float,
                    d_v: int = D_V, *, kv_format: str = "bf16", num_splits: int = 0,
-                   b_topk: int = 0, out: torch.Tensor | None = None,
+                   b_topk: int = 0, schedule: str = "auto", persistent_workgroups: int = 0,
+                   out: torch.Tensor | None = None,
                    lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                    stream: int | None = None, block_table: torch.Tensor | None = None,
                    page_size: int | None = None):
@@ -126,7 +129,10 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
     uint8 [s_kv, 640] packed rows (see ``pack_fp8_kv``), or with
     ``kv_format="fp4"`` uint8 [s_kv, 320] (see ``pack_fp4_kv``); indices: int32
     [s_q, topk].  Every tensor must be on q's device (pack the quantised rows
-    with ``device=``).  ``num_splits``/``b_topk`` 0 let the library plan.
+    with ``device=``).  ``num_splits``/``b_topk`` 0 let the library plan;
+    ``schedule`` is ``"auto"``, ``"grid"`` (one workgroup per token, split
+    and head group) or ``"persistent"`` (``persistent_workgroups`` workgroups,
+    0 = one per compute unit, on runs of tokens of equal block weight).
     Outputs and the split workspace are allocated with torch unless given.
 
     Paged KV: ``block_table`` int32 [s_q, table_width] and ``page_size``; kv is
@@ -149,8 +155,10 @@ def sparse_mla_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_
         out = torch.empty((s_q, h_q, d_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((s_q, h_q), dtype=torch.float32, device=q.device)
+    sched = {"auto": SMLA_SCHEDULE_AUTO, "grid": SMLA_SCHEDULE_GRID,
+             "persistent": SMLA_SCHEDULE_PERSISTENT}[schedule]
     p = make_params(q, kv, indices, sm_scale, out, lse, kv_format=fmt, num_splits=num_splits,
-                    b_topk=b_topk)
+                    b_topk=b_topk, schedule=sched, persistent_workgroups=persistent_workgroups)
     paged = make_paged(block_table, page_size) if block_table is not None else None
     need = smla_fwd_workspace_size(p) if paged is None else smla_fwd_paged_workspace_size(p, paged)
     if need:

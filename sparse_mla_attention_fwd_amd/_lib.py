@@ -19,6 +19,9 @@ SMLA_ERR_INVALID_ARGUMENT = 1
 SMLA_ERR_UNSUPPORTED = 2
 SMLA_ERR_WORKSPACE = 3
 SMLA_ERR_HIP = 4
+SMLA_SCHEDULE_AUTO = 0
+SMLA_SCHEDULE_GRID = 1
+SMLA_SCHEDULE_PERSISTENT = 2
 SMLA_KV_BF16 = 0
 SMLA_KV_FP8_E4M3 = 1
 SMLA_KV_FP4_E2M1 = 2
@@ -32,11 +35,11 @@ MAX_SLOTS_PER_SPLIT = 2048
 MAX_SLOTS_PER_SPLIT_FP8 = 1536
 
 # Every symbol include/smla.h declares.
-EXPORTS = ("smla_fwd_plan", "smla_fwd_workspace_size", "smla_fwd", "smla_fwd_static_scratch",
+EXPORTS = ("smla_fwd_plan", "smla_fwd_schedule", "smla_fwd_workspace_size", "smla_fwd", "smla_fwd_static_scratch",
            "smla_fwd_paged_workspace_size",
            "smla_fwd_paged", "smla_fwd_tune_workspace_size", "smla_fwd_tune", "smla_pack_fp8_kv_host",
            "smla_pack_fp4_kv_host", "smla_status_string", "smla_last_error", "smla_abi_version")
-ABI_VERSION = 5
+ABI_VERSION = 6
 STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -52,6 +55,7 @@ class smla_fwd_params(ctypes.Structure):
         ("out_stride_head", ctypes.c_int64),
         ("lse", ctypes.c_void_p), ("lse_stride_token", ctypes.c_int64),
         ("num_splits", ctypes.c_int32), ("b_topk", ctypes.c_int32),
+        ("schedule", ctypes.c_int32), ("persistent_workgroups", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -83,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.POINTER(smla_fwd_params)
     lib.smla_fwd_plan.argtypes = [P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.smla_fwd_plan.restype = ctypes.c_int
+    lib.smla_fwd_schedule.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+    lib.smla_fwd_schedule.restype = ctypes.c_int
     lib.smla_fwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.smla_fwd_workspace_size.restype = ctypes.c_int
     lib.smla_fwd.argtypes = [P, ctypes.c_void_p]
@@ -132,6 +138,14 @@ def smla_fwd_plan(params: smla_fwd_params) -> tuple[int, int]:
     ns, bt = ctypes.c_int32(), ctypes.c_int32()
     _check(load().smla_fwd_plan(ctypes.byref(params), ctypes.byref(ns), ctypes.byref(bt)))
     return ns.value, bt.value
+
+
+def smla_fwd_schedule(params: smla_fwd_params) -> int:
+    """SMLA_SCHEDULE_GRID or SMLA_SCHEDULE_PERSISTENT: the schedule the library
+    would run."""
+    v = ctypes.c_int32()
+    _check(load().smla_fwd_schedule(ctypes.byref(params), ctypes.byref(v)))
+    return v.value
 
 
 def smla_fwd_workspace_size(params: smla_fwd_params) -> int:
@@ -222,7 +236,8 @@ def smla_pack_fp4_kv_host(codes: torch.Tensor, scales: torch.Tensor) -> torch.Te
 
 def make_params(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_scale: float,
                 out: torch.Tensor, lse: torch.Tensor, *, kv_format: int = SMLA_KV_BF16,
-                s_kv: int | None = None, num_splits: int = 0, b_topk: int = 0) -> smla_fwd_params:
+                s_kv: int | None = None, num_splits: int = 0, b_topk: int = 0, schedule: int = 0,
+                persistent_workgroups: int = 0) -> smla_fwd_params:
     """Fill smla_fwd_params from tensors (no checks beyond shapes: the library
     validates everything else)."""
     s_q, h_q, d_qk = q.shape
@@ -239,4 +254,5 @@ def make_params(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, sm_sca
     p.out, p.out_stride_token, p.out_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
     p.lse, p.lse_stride_token = lse.data_ptr(), lse.stride(0)
     p.num_splits, p.b_topk = num_splits, b_topk
+    p.schedule, p.persistent_workgroups = schedule, persistent_workgroups
     return p

@@ -39,8 +39,22 @@ struct Plan {
   int32_t num_splits;
   int32_t b_topk;
   int32_t slots_per_split;
+  bool persistent;          // persistent schedule
+  bool block_counts;        // per-token block counts computed ahead, into the workspace
   size_t workspace_bytes;
 };
+
+
+// Bytes of KV reachable with 32-bit offsets from the KV base: (s_kv - 1) *
+// row stride + the row length when that is at most the buffer window, else 0.
+uint32_t kv_window_bytes(const smla_fwd_params* p) {
+  const int64_t row_bytes = p->kv_format == SMLA_KV_BF16 ? p->kv_stride_row * 2 : p->kv_stride_row;
+  const int64_t row_len = p->kv_format == SMLA_KV_BF16      ? 2 * SMLA_D_QK
+                          : p->kv_format == SMLA_KV_FP8_E4M3 ? SMLA_FP8_ROW_BYTES
+                                                             : SMLA_FP4_ROW_BYTES;
+  const int64_t window = p->s_kv > 0 ? (p->s_kv - 1) * row_bytes + row_len : 0;
+  return window > 0 && window <= (int64_t)smla::kDummyOffset ? (uint32_t)window : 0u;
+}
 
 // Decode occupancy: a token's topk range is cut so that the grid holds at least
 // about two workgroups per CU, with no part smaller than 64 slots and none
@@ -70,6 +84,11 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   if (p->b_topk != 0 && p->b_topk != 32 && p->b_topk != 64)
     return fail(SMLA_ERR_UNSUPPORTED, "b_topk=%d: supported 32, 64 (0 = auto)", p->b_topk);
   if (p->num_splits < 0) return fail(SMLA_ERR_INVALID_ARGUMENT, "num_splits=%d is negative", p->num_splits);
+  if (p->schedule < SMLA_SCHEDULE_AUTO || p->schedule > SMLA_SCHEDULE_PERSISTENT)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "schedule=%d unknown", p->schedule);
+  if (p->persistent_workgroups < 0 || p->persistent_workgroups > 65535)
+    return fail(SMLA_ERR_INVALID_ARGUMENT, "persistent_workgroups=%d outside [0, 65535]",
+                p->persistent_workgroups);
 
   if (p->s_q > 0) {
     if (!p->q || !p->kv || !p->indices || !p->out || !p->lse)
@@ -121,7 +140,8 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   if (ns == 0) {
     ns = min_splits;
     const int64_t units = (int64_t)p->s_q * (p->h_q > 64 ? p->h_q / 64 : 1);   // workgroups per split
-    if (units > 0 && units * ns < kTargetWorkgroups) {
+    // (the persistent schedule runs one split per token: no occupancy splits)
+    if (p->schedule != SMLA_SCHEDULE_PERSISTENT && units > 0 && units * ns < kTargetWorkgroups) {
       const int32_t want = (int32_t)((kTargetWorkgroups + units - 1) / units);
       const int32_t cap = (p->topk + 63) / 64;   // parts of at least 64 slots
       ns = want < cap ? want : cap;
@@ -145,12 +165,53 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
                                                                                                       : 32;
   if ((int64_t)p->s_q * pl.num_splits * (p->h_q > 64 ? 2 : 1) + 8 > 2147483647LL)
     return fail(SMLA_ERR_UNSUPPORTED, "grid of s_q*num_splits workgroups is too large");
+  // Persistent schedule: bf16 KV in the 32-bit window, 64 heads, one split of
+  // the pipelined kernel's length, B_TOPK 32.
+  const bool can_persist = p->kv_format == SMLA_KV_BF16 && p->h_q == 64 && pl.num_splits == 1 &&
+                           pl.slots_per_split >= smla::kPipeMinSlots && pl.b_topk == 32 &&
+                           kv_window_bytes(p) != 0 && p->s_q <= (1 << 24);
+  if (p->schedule == SMLA_SCHEDULE_PERSISTENT && !can_persist)
+    return fail(SMLA_ERR_UNSUPPORTED,
+                "persistent schedule: built for bf16 KV within 4 GB, h_q 64, one split, topk >= %d "
+                "and b_topk 32", smla::kPipeMinSlots);
+  pl.persistent = can_persist && p->schedule == SMLA_SCHEDULE_PERSISTENT;
+  // One split of the pipelined kernel in the 32-bit window: each token's
+  // block count is computed ahead by one pass over the index rows, so that a
+  // workgroup starts its gathers without scanning its row first.
+  pl.block_counts = pl.persistent || (p->kv_format == SMLA_KV_BF16 && p->h_q >= 64 && pl.num_splits == 1 &&
+                                      pl.slots_per_split >= smla::kPipeMinSlots && pl.b_topk == 32 &&
+                                      kv_window_bytes(p) != 0 && p->s_q <= (1 << 24));
   pl.workspace_bytes = 0;
   if (pl.num_splits > 1) {
     const size_t parts = (size_t)p->s_q * pl.num_splits * p->h_q;
     pl.workspace_bytes = parts * SMLA_D_V * sizeof(uint16_t) + ((parts * sizeof(float) + 255) & ~size_t(255));
+  } else if (pl.block_counts) {
+    pl.workspace_bytes = ((size_t)p->s_q * sizeof(int32_t) + 255) & ~size_t(255);
   }
   *plan = pl;
+  return SMLA_OK;
+}
+
+// Compute units of the device that runs `stream`, queried once per device.
+constexpr int kMaxDevicesCu = 64;
+std::mutex g_cu_mutex;
+int g_cu_count[kMaxDevicesCu] = {};
+
+smla_status compute_units(hipStream_t stream, int* out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevicesCu)
+    return fail(SMLA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevicesCu);
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n < 1)
+      return fail(SMLA_ERR_HIP, "compute units of device %d: %s", dev, hipGetErrorString(e));
+    g_cu_count[dev] = n;
+  }
+  *out = g_cu_count[dev];
   return SMLA_OK;
 }
 
@@ -191,12 +252,23 @@ smla_status launch_plan(const smla_fwd_params* p, const Plan& pl, const int32_t*
   }
   a.s_kv = p->s_kv;
   a.scale_log2 = p->sm_scale * 1.4426950408889634f;
-  {
-    const int64_t row_len = p->kv_format == SMLA_KV_BF16      ? 2 * SMLA_D_QK
-                            : p->kv_format == SMLA_KV_FP8_E4M3 ? SMLA_FP8_ROW_BYTES
-                                                               : SMLA_FP4_ROW_BYTES;
-    const int64_t window = p->s_kv > 0 ? (p->s_kv - 1) * a.kv_row_bytes + row_len : 0;
-    a.kv_window_bytes = window > 0 && window <= (int64_t)smla::kDummyOffset ? (uint32_t)window : 0u;
+  a.kv_window_bytes = kv_window_bytes(p);
+  a.token_blocks = nullptr;
+  if (pl.block_counts) {
+    int32_t* nb = reinterpret_cast<int32_t*>(split_ws);
+    hipError_t e = smla::launch_token_blocks(a, nb, stream);
+    if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    a.token_blocks = nb;
+    if (pl.persistent) {
+      int grid = p->persistent_workgroups;
+      if (grid == 0) {
+        const smla_status cs = compute_units(stream, &grid);
+        if (cs != SMLA_OK) return cs;
+      }
+      e = smla::launch_bf16_persist(a, grid, stream);
+      if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+      return SMLA_OK;
+    }
   }
   const hipError_t e = smla::launch_fwd(a, pl.b_topk, p->kv_format, stream);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -295,6 +367,15 @@ smla_status smla_fwd_plan(const smla_fwd_params* p, int32_t* num_splits, int32_t
   if (s != SMLA_OK) return s;
   if (num_splits) *num_splits = pl.num_splits;
   if (b_topk) *b_topk = pl.b_topk;
+  return SMLA_OK;
+}
+
+smla_status smla_fwd_schedule(const smla_fwd_params* p, int32_t* schedule) {
+  if (!schedule) return fail(SMLA_ERR_INVALID_ARGUMENT, "schedule is NULL");
+  Plan pl;
+  const smla_status s = check_and_plan(p, &pl);
+  if (s != SMLA_OK) return s;
+  *schedule = pl.persistent ? SMLA_SCHEDULE_PERSISTENT : SMLA_SCHEDULE_GRID;
   return SMLA_OK;
 }
 

@@ -270,6 +270,9 @@ __global__ __launch_bounds__(256) void smla_fwd_fp8_pipe_kernel(FwdArgs a) {
   // land while the remaining PV MFMAs run
   auto soft_step = [&](auto K, Soft& sm, const QkOut& qo, const f32x4 (&bias)[KT], const f32x4 (&sc4)[KT][4],
                        int p) __attribute__((always_inline)) {
+    // no contraction across the steps (the running state rounds the same way
+    // wherever the compiler places the steps)
+#pragma clang fp contract(off)
     constexpr int k = decltype(K)::value;
     if constexpr (k == 0) {
       // an invalid slot's bias of -inf masks it; a valid slot's 0 changes nothing

@@ -6,8 +6,6 @@
 
 namespace smla {
 
-// Slots per split from which the pipelined kernel is used.
-constexpr int kPipeMinSlots = 1024;
 // Raw-row stages of the pipelined fp8 kernel.
 constexpr int kFp8Stages = 6;
 
@@ -19,7 +17,9 @@ hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
     // kernel (its prologue costs more; short decode splits keep the other one)
     if (a.slots_per_split >= kPipeMinSlots) {
       const dim3 grid(grid_size(a)), block(256);
-      if (split && buf)
+      if (a.token_blocks)   // one split, 32-bit window, block counts computed ahead
+        hipLaunchKernelGGL((smla_fwd_bf16_pipe_kernel<false, true, true>), grid, block, 0, stream, a);
+      else if (split && buf)
         hipLaunchKernelGGL((smla_fwd_bf16_pipe_kernel<true, true>), grid, block, 0, stream, a);
       else if (split)
         hipLaunchKernelGGL((smla_fwd_bf16_pipe_kernel<true, false>), grid, block, 0, stream, a);

@@ -14,6 +14,9 @@ constexpr int kRowBytesBf16 = kDqk * 2;   // 1152: nine 128-byte lines
 constexpr int kFp8RowBytes = 640;         // 576 codes + 5 float32 scales + pad
 constexpr int kFp4RowBytes = 320;         // 288 bytes of two codes each + 5 float32 scales + pad
 constexpr int kMaxSlotsPerSplit = 2048;
+// Slots per split from which the pipelined 64-head bf16 kernel runs (and the
+// persistent schedule, which is built on it, may)
+constexpr int kPipeMinSlots = 1024;
 // fp8 KV: the raw-row ring and two bf16 stages leave room for 1536 indices
 constexpr int kMaxSlotsPerSplitFp8 = 1536;
 // Buffer-load offset past every KV window: a gather for a block past the end
@@ -50,6 +53,10 @@ struct FwdArgs {
   // loads, whose hardware range check also covers every access), else 0 (the
   // gathers use 64-bit global addresses).
   uint32_t kv_window_bytes;
+  // Blocks of each token up to its last valid slot (at least 1), computed by
+  // a pass over the index rows before the forward kernel (single-split plans
+  // in the 32-bit window; else null and each workgroup scans its own slots).
+  const int32_t* token_blocks;
 };
 
 // KV row formats (the values of smla_kv_format).
@@ -65,6 +72,15 @@ hipError_t launch_paged_translate(const int32_t* idx, int64_t idx_st, const int3
                                   int64_t bt_st, int32_t table_width, int32_t page_size,
                                   int64_t num_pages, int32_t s_q, int32_t topk, int32_t* phys,
                                   hipStream_t stream);
+
+// Per-token block counts (blocks up to the token's last valid slot, at least
+// 1) into nb [s_q] (device scratch).
+hipError_t launch_token_blocks(const FwdArgs& a, int32_t* nb, hipStream_t stream);
+
+// Persistent schedule (bf16 KV, 64 heads, one split per token, KV within the
+// 32-bit window; a.token_blocks set): `grid` persistent workgroups, each on a
+// contiguous run of tokens of about equal block weight.
+hipError_t launch_bf16_persist(const FwdArgs& a, int grid, hipStream_t stream);
 
 // Forward kernel launchers per configuration (NW = waves per workgroup =
 // heads per workgroup / 16; BT = B_TOPK), each instantiated in its own

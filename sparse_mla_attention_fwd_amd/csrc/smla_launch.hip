@@ -79,7 +79,42 @@ __global__ __launch_bounds__(256) void smla_paged_translate_kernel(
   phys[i] = r;
 }
 
+// Blocks of each token up to its last valid slot, at least 1 (an empty
+// token still takes one fully masked block): one wave per token reads the
+// token's index row.
+__global__ __launch_bounds__(256) void smla_token_blocks_kernel(const int32_t* __restrict__ idx, int64_t idx_st,
+                                                                int32_t s_q, int32_t topk, int64_t s_kv,
+                                                                int32_t* __restrict__ nb) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= s_q) return;
+  const int32_t* __restrict__ irow = idx + t * idx_st;
+  int last = -1;
+  int j = lane;
+  for (; j + 7 * 64 < topk; j += 8 * 64) {
+    int v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = irow[j + 64 * k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (v[k] >= 0 && (int64_t)v[k] < s_kv) last = j + 64 * k;
+  }
+  for (; j < topk; j += 64) {
+    const int v = irow[j];
+    if (v >= 0 && (int64_t)v < s_kv) last = j;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off));
+  if (lane == 0) nb[t] = last < 0 ? 1 : last / 32 + 1;
+}
+
 }  // namespace
+
+hipError_t launch_token_blocks(const FwdArgs& a, int32_t* nb, hipStream_t stream) {
+  hipLaunchKernelGGL(smla_token_blocks_kernel, dim3((unsigned)((a.s_q + 3) / 4)), dim3(256), 0, stream, a.idx,
+                     a.idx_st, a.s_q, a.topk, a.s_kv, nb);
+  return hipGetLastError();
+}
 
 hipError_t launch_paged_translate(const int32_t* idx, int64_t idx_st, const int32_t* block_table,
                                   int64_t bt_st, int32_t table_width, int32_t page_size,

@@ -312,3 +312,37 @@ def test_static_scratch_size_and_oversized_plans():
         assert "static scratch" in _lib.last_error()
         bad = _params(h_q=24)
         assert lib.smla_fwd_static_scratch(ctypes.byref(bad), None) == _lib.SMLA_ERR_UNSUPPORTED
+
+
+def test_schedule_planning():
+    """The planner runs the grid; single-split pipelined plans in the 32-bit
+    window take one int32 block count per token of workspace (computed ahead);
+    the persistent schedule runs when asked for and is refused where it is not
+    built."""
+    big = dict(s_q=4096, h_q=64, topk=2048, s_kv=65536, indices_stride_token=2048,
+               q_stride_token=64 * 576, out_stride_token=64 * 512, lse_stride_token=64)
+    p = _params(**big)
+    assert _lib.smla_fwd_schedule(p) == _lib.SMLA_SCHEDULE_GRID
+    assert _lib.smla_fwd_plan(p) == (1, 32)
+    assert _lib.smla_fwd_workspace_size(p) == 4096 * 4
+    p = _params(**big, schedule=_lib.SMLA_SCHEDULE_PERSISTENT)
+    assert _lib.smla_fwd_schedule(p) == _lib.SMLA_SCHEDULE_PERSISTENT
+    assert _lib.smla_fwd_workspace_size(p) == 4096 * 4
+    p = _params(**dict(big, s_kv=4_000_000))                # beyond the 32-bit window: no counts
+    assert _lib.smla_fwd_workspace_size(p) == 0
+    p = _params(**dict(big, topk=512, indices_stride_token=512), num_splits=1)   # short split
+    assert _lib.smla_fwd_workspace_size(p) == 0
+    p = _params(**dict(big, s_q=3), schedule=_lib.SMLA_SCHEDULE_PERSISTENT, persistent_workgroups=2)
+    assert _lib.smla_fwd_schedule(p) == _lib.SMLA_SCHEDULE_PERSISTENT
+    assert _lib.smla_fwd_workspace_size(p) == 256
+    for bad in (dict(h_q=128, q_stride_token=128 * 576, out_stride_token=128 * 512, lse_stride_token=128),
+                dict(topk=1000, indices_stride_token=1000), dict(b_topk=64), dict(num_splits=2),
+                dict(kv_format=1, kv_stride_row=640), dict(s_kv=4_000_000)):
+        p = _params(**dict(big, **bad), schedule=_lib.SMLA_SCHEDULE_PERSISTENT)
+        with pytest.raises(_lib.SmlaError):
+            _lib.smla_fwd_schedule(p)
+    for field, value in (("schedule", 3), ("schedule", -1), ("persistent_workgroups", -1),
+                         ("persistent_workgroups", 1 << 16)):
+        p = _params(**{field: value})
+        with pytest.raises(_lib.SmlaError):
+            _lib.smla_fwd_plan(p)

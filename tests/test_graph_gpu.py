@@ -28,6 +28,10 @@ def _inputs(kind):
     if kind == "bf16_split":
         x = workloads.make_random(s_q=16, h_q=128, topk=512, s_kv=8192, seed=71, invalid_frac=0.1)
         kw = dict(num_splits=4)
+    elif kind == "persistent":
+        x = workloads.make_random(s_q=20, h_q=64, topk=1100, s_kv=6000, seed=74, invalid_frac=0.2)
+        x["indices"][3, :] = -1
+        kw = dict(schedule="persistent", persistent_workgroups=4)
     elif kind == "paged":
         x = workloads.make_random_paged(s_q=8, h_q=64, topk=700, page_size=16, num_pages=80,
                                         table_width=64, seed=72, unallocated_frac=0.1)
@@ -45,7 +49,7 @@ def _inputs(kind):
     return q, kv, idx, x["sm_scale"], kw
 
 
-@pytest.mark.parametrize("kind", ["bf16_split", "paged", "fp8", "fp4"])
+@pytest.mark.parametrize("kind", ["bf16_split", "persistent", "paged", "fp8", "fp4"])
 def test_graph_replays_match_eager(smla, kind):
     q, kv, idx, sm_scale, kw = _inputs(kind)
     dev = q.device

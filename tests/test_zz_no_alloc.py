@@ -23,7 +23,7 @@ def lib():
     return _lib
 
 
-def _call(_lib, x, num_splits, kv_format="bf16"):
+def _call(_lib, x, num_splits, kv_format="bf16", **extra):
     """(static-scratch result, workspace result) of one configuration."""
     import sparse_mla_attention_fwd_amd as smla
     dev = torch.device("cuda:0")
@@ -37,7 +37,8 @@ def _call(_lib, x, num_splits, kv_format="bf16"):
     for static in (True, False):
         out = torch.full((s_q, h_q, 512), float("nan"), dtype=torch.bfloat16, device=dev)
         lse = torch.full((s_q, h_q), float("nan"), dtype=torch.float32, device=dev)
-        p = _lib.make_params(q, kv, idx, x["sm_scale"], out, lse, kv_format=fmt, num_splits=num_splits)
+        p = _lib.make_params(q, kv, idx, x["sm_scale"], out, lse, kv_format=fmt, num_splits=num_splits,
+                             **extra)
         need = _lib.smla_fwd_workspace_size(p)
         assert 0 < need <= _lib.STATIC_SCRATCH_BYTES
         stream = torch.cuda.current_stream().cuda_stream
@@ -85,3 +86,13 @@ def test_static_scratch_fp8_and_single_split(lib):
     ref = smla.sparse_mla_fwd(q, kv, idx, y["sm_scale"], num_splits=1)
     torch.cuda.synchronize()
     assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+
+
+def test_static_scratch_persistent_schedule(lib):
+    """The persistent schedule keeps its per-token block counts in the scratch."""
+    x = workloads.make_random(s_q=30, h_q=64, topk=1100, s_kv=5000, seed=505, invalid_frac=0.2)
+    x["indices"][4, :] = -1
+    (so, sl), (wo, wl) = _call(lib, x, 1, schedule=lib.SMLA_SCHEDULE_PERSISTENT, persistent_workgroups=5)
+    assert torch.equal(so, wo) and torch.equal(sl, wl)
+    ro, rl = oracle_tokens(x)
+    check(so.float().cpu().numpy(), sl.cpu().numpy().astype(np.float64), ro, rl, "static persistent")
