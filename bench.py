@@ -6,8 +6,10 @@ A step is one forward pass over the whole workload (every token, every
 head): one call of the library's entry point, which launches the fused
 kernel (plus the split combine for decode plans).  Inputs are resident in HBM
 before the timed region.  Before every timed step a 512 MiB scratch buffer is
-written (outside the step's events), so that neither the L2 nor the 256 MB
-MALL holds anything of the inputs from the previous step; the step itself is
+written and then read back (outside the step's events), so that neither the
+L2 nor the 256 MB MALL holds anything of the inputs from the previous step,
+and the caches hold only clean lines (a write alone leaves the MALL full of
+dirty lines, whose write-back the next step would pay for); the step itself is
 bracketed by HIP events on its stream, and the median over the K steps is the
 step time.  The K steps with their flushes run between two device
 synchronisations.  Prints one JSON line.
@@ -308,8 +310,9 @@ def main():
         torch.cuda.synchronize()
 
     # Per-step durations with events on the launch stream.  Before each step a
-    # scratch buffer larger than the MALL is written (outside the events), so
-    # the step finds its inputs in HBM, not in a cache warmed by the last step.
+    # scratch buffer larger than the MALL is written and read back (outside
+    # the events), so the step finds its inputs in HBM, not in a cache warmed
+    # by the last step, and no dirty flush lines are left for it to evict.
     flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -318,6 +321,7 @@ def main():
     for i in range(args.steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
+            flush.view(torch.int32).amax()
         starts[i].record(stream)
         step()
         ends[i].record(stream)

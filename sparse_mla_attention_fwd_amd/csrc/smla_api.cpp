@@ -62,9 +62,6 @@ uint32_t kv_window_bytes(const smla_fwd_params* p) {
 // Workgroups a split plan aims for: one per compute unit (the forward kernels
 // hold more than half of a unit's LDS, so one workgroup is resident per unit).
 constexpr int kTargetWorkgroups = 256;
-// Slots the bf16 gather ring of the non-pipelined kernel holds at once (four
-// stages of 32 rows, or two of 64).
-constexpr int32_t kRingSlots = 128;
 
 smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   if (!p) return fail(SMLA_ERR_INVALID_ARGUMENT, "params is NULL");
@@ -244,9 +241,9 @@ smla_status launch_plan(const smla_fwd_params* p, const Plan& pl, const int32_t*
   a.num_splits = pl.num_splits;
   a.head_groups = p->h_q > 64 ? p->h_q / 64 : 1;
   a.inner_groups = 1;
-  if (p->kv_format == SMLA_KV_BF16 && p->h_q > 64 && pl.slots_per_split <= kRingSlots) {
-    // Every block of a split fits in the gather ring at once: one workgroup
-    // gathers the rows once and runs all head groups over them.
+  if (p->kv_format == SMLA_KV_BF16 && p->h_q > 64 && pl.slots_per_split <= smla::kShortSlots) {
+    // A short split is one block resident in LDS: one workgroup gathers the
+    // rows once and runs both head groups over them.
     a.inner_groups = a.head_groups;
     a.head_groups = 1;
   }

@@ -496,6 +496,291 @@ __device__ __forceinline__ void write_output(const FwdArgs& a, State& st, int to
   }
 }
 
+// Compaction of index values already loaded (C per thread: slot
+// lo + c·NT + tid, -1 past the split), as compact_slots.
+template <int NW, int C>
+__device__ int compact_values(const int (&v)[C], int64_t s_kv, int* sidx, int* swcnt, int tid) {
+  const int lane = tid & 63, w = tid >> 6;
+  int nvalid = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const bool ok = v[c] >= 0 && (int64_t)v[c] < s_kv;
+    const uint64_t m = __ballot(ok);
+    const int pre = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) swcnt[w] = __popcll(m);
+    __syncthreads();
+    int base = nvalid, tot = 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+      const int cnt = swcnt[u];
+      if (u < w) base += cnt;
+      tot += cnt;
+    }
+    if (ok) sidx[base + pre] = v[c];
+    nvalid += tot;
+    __syncthreads();
+  }
+  return nvalid;
+}
+
+// Output row of a head (the output, or the split partial) and its lse slot.
+template <bool SPLIT>
+__device__ __forceinline__ uint16_t* out_row(const FwdArgs& a, int token, int split, int head, float*& lse) {
+  if constexpr (!SPLIT) {
+    lse = a.lse + (int64_t)token * a.lse_st + head;
+    return a.out + (int64_t)token * a.out_st + (int64_t)head * a.out_sh;
+  } else {
+    const int64_t part = ((int64_t)token * a.num_splits + split) * a.h_q + head;
+    lse = a.ws_lse + part;
+    return a.ws_o + part * kDv;
+  }
+}
+
+// Short splits (at most 128 slots: decode with the topk range cut into
+// parts) as ONE block of B_TOPK = 128 (page "Ascend Sparse Attention Forward
+// 算法与优化技术简析", section 计算流程: the block loop of the online softmax
+// with a single block, so running_max_for_softmax is the block's max and no
+// rescale can occur).  The 128 rows fill four 32-row stages of LDS at once.
+//   * The split's indices are loaded first, then Q: compaction waits only
+//     for the indices.  Every slot past the valid count repeats the first
+//     valid row (finite, weight 0), so all four stages hold real rows.
+//   * QKᵀ runs stage by stage, each stage after its own rows have arrived;
+//     the logits of all 128 slots stay in registers, then one softmax pass.
+//   * With NG = 2 (h_q = 128) a wave owns 16 heads of each 64-head group:
+//     every K and V operand read from LDS feeds the MFMAs of both groups,
+//     which halves the LDS operand traffic (the products' bound with one
+//     wave per SIMD).  Both groups' Q (registers) are live in QKᵀ only, both
+//     output accumulators (AGPRs) in PV only.
+template <int NW, bool SPLIT, bool BUF, int NG>
+__global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_short_kernel(FwdArgs a) {
+  constexpr int BT = 32, NST = 4, MAXS = BT * NST;
+  constexpr int LPB = loads_per_block<NW, BT>();
+  constexpr int TILE = BT * kRowBytesBf16;
+  constexpr int NT = NW * 64;
+  constexpr int C = (MAXS + NT - 1) / NT;
+  constexpr int KT = MAXS / 16;                 // key tiles of 16 slots
+  constexpr int UNIT_GROUP = (BT / 8) * 1024;   // bytes between chunk groups of a stage
+  __shared__ __attribute__((aligned(1024))) char st0[TILE];
+  __shared__ __attribute__((aligned(1024))) char st1[TILE];
+  __shared__ __attribute__((aligned(1024))) char st2[TILE];
+  __shared__ __attribute__((aligned(1024))) char st3[TILE];
+  __shared__ int sidx[MAXS];
+  __shared__ int swcnt[NW];
+  char* const stages[4] = {st0, st1, st2, st3};
+
+  WorkItem wi;
+  if (!work_item(a, wi)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int token = wi.token, split = wi.split;
+  const int lo = split * a.slots_per_split;
+  const int hi = min(a.topk, lo + a.slots_per_split);
+
+  const int32_t* irow = a.idx + (int64_t)token * a.idx_st;
+  int v[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int j = lo + c * NT + tid;
+    v[c] = j < hi ? irow[j] : -1;
+  }
+  const int head = wi.head0 + w * 16 + n;
+  const int nvalid = compact_values<NW, C>(v, a.s_kv, sidx, swcnt, tid);
+
+  if (nvalid == 0) {
+    // no valid slot: out = 0, lse = −∞ (every group)
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) {
+      float* lse;
+      uint16_t* row = out_row<SPLIT>(a, token, split, head + 64 * gr, lse);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) *(i32x4*)(row + 32 * k + 8 * g) = i32x4{0, 0, 0, 0};
+      if (g == 0) *lse = kNegInf;
+    }
+    return;
+  }
+  for (int j = nvalid + tid; j < MAXS; j += NT) sidx[j] = sidx[0];
+  __syncthreads();
+
+  // Stage 0's gathers, then Q, then stages 1..3 (loads complete in issue
+  // order, so the wait for stage b covers Q from b = 0 on).  Q is not loaded
+  // before the indices: the whole chip issues these bursts at once, and Q
+  // traffic ahead of the index loads delays every workgroup's indices.
+  const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
+  const KvSource<BUF> src(a.kv, a.kv_window_bytes);
+  bf16x8 q0[18], q1[18];
+  static_for<0, NST>([&](auto B) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    GatherPlan<NW, BT, BUF> gp;
+    gp.prepare(stages[b], src, a.kv_row_bytes, sidx + b * BT, tid);
+    gp.issue_all();
+    if constexpr (b == 0) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      load_q(a, token, head, g, q0);
+      if constexpr (NG == 2) load_q(a, token, head + 64, g, q1);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  });
+
+  // ---- Pᵀ = G·Qᵀ, stage by stage.  Key tile 2b + kt of stage b; even and
+  // odd steps of a stage accumulate separately (more independent chains).
+  constexpr int PF = 12;                        // K operand reads in flight
+  f32x4 p[NG][KT];
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) p[gr][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto qk_off = [&](int i) __attribute__((always_inline)) {
+    const int s = i / 2, kt = i % 2;
+    return lofs.qk[s & 1] + (s >> 1) * UNIT_GROUP + kt * 2048;
+  };
+  static_for<0, NST>([&](auto B) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    const char* tile = stages[b];
+    wait_vm_lgkm0<(NST - 1 - b) * LPB>();
+    barrier_no_vm_drain();
+    f32x4 odd[NG][2];
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) odd[gr][0] = odd[gr][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 abuf[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) abuf[i] = lds_load<bf16x8>(tile, qk_off(i));
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 36>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value, s = i / 2, kt = i % 2;
+      if constexpr (s % 2 == 0) {
+        p[0][2 * b + kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], q0[s], p[0][2 * b + kt], 0, 0, 0);
+        if constexpr (NG == 2)
+          p[1][2 * b + kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], q1[s], p[1][2 * b + kt], 0, 0, 0);
+      } else {
+        odd[0][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], q0[s], odd[0][kt], 0, 0, 0);
+        if constexpr (NG == 2)
+          odd[1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], q1[s], odd[1][kt], 0, 0, 0);
+      }
+      if constexpr (i + PF < 36) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) p[gr][2 * b + kt] += odd[gr][kt];
+  });
+
+  // ---- softmax over the block: scaled logits in log2 units, slots past the
+  // valid count masked; running_max_for_softmax = the block's max (finite:
+  // slot 0 is valid), S = exp2(x - max), running_sumexp = Σ S (fp32, before
+  // the bf16 cast of S).
+  bf16x8 sb[NG][NST];
+  float msoft[NG], lsum[NG];
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr) {
+    float x[KT][4];
+    float cur = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float val = p[gr][kt][r] * a.scale_log2;
+        x[kt][r] = (16 * kt + 4 * g + r < nvalid) ? val : kNegInf;
+        cur = fmaxf(cur, x[kt][r]);
+      }
+    const float m = wave_max16x4(cur);
+    float sum = 0.f;
+    float sv[KT][4];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[kt][r] = __builtin_amdgcn_exp2f(x[kt][r] - m);
+        sum += sv[kt][r];
+      }
+    msoft[gr] = m;
+    lsum[gr] = wave_sum16x4(sum);
+    // B operand of key step b (stage b): keys 32b + 4g + e and 32b + 16 + 4g + e
+#pragma unroll
+    for (int b = 0; b < NST; ++b) {
+      union { uint32_t u[4]; bf16x8 v; } t;
+      t.u[0] = pack2_bf16(sv[2 * b][0], sv[2 * b][1]);
+      t.u[1] = pack2_bf16(sv[2 * b][2], sv[2 * b][3]);
+      t.u[2] = pack2_bf16(sv[2 * b + 1][0], sv[2 * b + 1][1]);
+      t.u[3] = pack2_bf16(sv[2 * b + 1][2], sv[2 * b + 1][3]);
+      sb[gr][b] = t.v;
+    }
+  }
+
+  // ---- Oᵀ = Vᵀ·Sᵀ in chunks of four d_v tiles: a chunk accumulates over the
+  // four stages (key steps), then its tiles are final: normalised, packed and
+  // stored while the next chunks' products run, so the output stores are
+  // spread over PV instead of one burst at the end.  Each V fragment feeds
+  // both groups.
+  float* lsep[NG];
+  uint16_t* rowp[NG];
+  float inv[NG];
+#pragma unroll
+  for (int gr = 0; gr < NG; ++gr) {
+    rowp[gr] = out_row<SPLIT>(a, token, split, head + 64 * gr, lsep[gr]);
+    rowp[gr] += (g & 1) ? 16 + 4 * (g - 1) : 4 * g;
+    inv[gr] = 1.0f / lsum[gr];
+    if (g == 0) *lsep[gr] = (msoft[gr] + __builtin_amdgcn_logf(lsum[gr])) * kLn2;
+  }
+  constexpr int PFV = 6;                        // V fragments (two reads each) in flight
+  auto tr_load = [&](int b, int off) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)stages[b] + off));
+  };
+  // fragment f: chunk f / 16, stage (f / 4) % 4, tile dt = 4·chunk + f % 4
+  auto frag_off = [&](int f) __attribute__((always_inline)) {
+    const int dt = 4 * (f / 16) + f % 4;
+    return lofs.tr[dt & 3] + (dt >> 2) * UNIT_GROUP;
+  };
+  i16x4 va[PFV], vb[PFV];
+  static_for<0, PFV>([&](auto F) __attribute__((always_inline)) {
+    constexpr int f = decltype(F)::value;
+    va[f] = tr_load((f / 4) % 4, frag_off(f));
+    vb[f] = tr_load((f / 4) % 4, frag_off(f) + 2048);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<0, 8>([&](auto Q) __attribute__((always_inline)) {
+    constexpr int ch = decltype(Q)::value;
+    f32x4 o[NG][4];
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[gr][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_for<0, 16>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value, f = 16 * ch + i, b = i / 4, j = i % 4;
+      union { i16x4 h[2]; bf16x8 v; } av;
+      av.h[0] = va[f % PFV];
+      av.h[1] = vb[f % PFV];
+      o[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, sb[0][b], o[0][j], 0, 0, 0);
+      if constexpr (NG == 2)
+        o[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, sb[1][b], o[1][j], 0, 0, 0);
+      if constexpr (f + PFV < 128) {
+        va[f % PFV] = tr_load(((f + PFV) / 4) % 4, frag_off(f + PFV));
+        vb[f % PFV] = tr_load(((f + PFV) / 4) % 4, frag_off(f + PFV) + 2048);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // tiles 4ch .. 4ch+3 are final: pairs (4ch, 4ch+1) and (4ch+2, 4ch+3)
+    // give stores 2ch and 2ch+1 (16 bytes per lane, 64 contiguous bytes per
+    // head: rows 0<->1 and 2<->3 of the pair swapped)
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const f32x4 oe = o[gr][2 * k], oo = o[gr][2 * k + 1];
+        const float iv = inv[gr];
+        const uint32_t e0 = pack2_bf16(oe[0] * iv, oe[1] * iv), e1 = pack2_bf16(oe[2] * iv, oe[3] * iv);
+        const uint32_t o0 = pack2_bf16(oo[0] * iv, oo[1] * iv), o1 = pack2_bf16(oo[2] * iv, oo[3] * iv);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(e0, o0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(e1, o1, false, false);
+        *(i32x4*)(rowp[gr] + 32 * (2 * ch + k)) = i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 template <int NW, int BT, int NST, bool SPLIT, bool BUF>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   constexpr int LPB = loads_per_block<NW, BT>();
@@ -859,8 +1144,20 @@ unsigned grid_size(const FwdArgs& a) {
 template <int NW, int BT, bool SPLIT, bool BUF>
 void launch_bf16_variant(const FwdArgs& a, hipStream_t stream) {
   constexpr int NST = BT == 32 ? 4 : 2;
-  hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, BUF>), dim3(grid_size(a)), dim3(NW * 64),
-                     0, stream, a);
+  const dim3 grid(grid_size(a)), block(NW * 64);
+  if (a.slots_per_split <= kShortSlots) {
+    // short split: one block of up to 128 slots (two head groups per wave
+    // when inner_groups is 2)
+    if constexpr (NW == 4) {
+      if (a.inner_groups == 2) {
+        hipLaunchKernelGGL((smla_fwd_bf16_short_kernel<NW, SPLIT, BUF, 2>), grid, block, 0, stream, a);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((smla_fwd_bf16_short_kernel<NW, SPLIT, BUF, 1>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, BUF>), grid, block, 0, stream, a);
+  }
 }
 
 template <int NW, bool SPLIT, bool BUF, class Fmt = KvFp8Format>

@@ -17,6 +17,9 @@ constexpr int kMaxSlotsPerSplit = 2048;
 // Slots per split from which the pipelined 64-head bf16 kernel runs (and the
 // persistent schedule, which is built on it, may)
 constexpr int kPipeMinSlots = 1024;
+// Slots per split up to which a bf16 split runs as one block in the short
+// kernel (four 32-row stages resident at once)
+constexpr int kShortSlots = 128;
 // fp8 KV: the raw-row ring and two bf16 stages leave room for 1536 indices
 constexpr int kMaxSlotsPerSplitFp8 = 1536;
 // Buffer-load offset past every KV window: a gather for a block past the end

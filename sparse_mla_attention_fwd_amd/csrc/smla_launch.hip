@@ -10,7 +10,12 @@ namespace smla {
 namespace {
 
 // Log-sum-exp merge of split partials (bf16 O/l and fp32 lse per part): one
-// thread per (token, head, 8 columns).
+// thread per (token, head, 8 columns).  Parts are merged four at a time: the
+// four lse values and partial rows of a chunk are all loaded before any is
+// used (one memory round trip per chunk), then folded into the running
+// merge with the chunk's max.  A part with lse = −∞ (no valid slot) gets
+// weight 0; its partial row, written as zeros, is still loaded, and loads
+// past the last part repeat the last part with weight 0.
 __global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.s_q * a.h_q * (kDv / 8);
@@ -21,26 +26,42 @@ __global__ __launch_bounds__(256) void smla_combine_kernel(FwdArgs a) {
   const int64_t token = th / a.h_q;
   const int ns = a.num_splits;
   const int64_t part0 = token * ns * a.h_q + head;
-  float m = kNegInf;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, a.ws_lse[part0 + (int64_t)s * a.h_q]);
+  float m = kNegInf, z = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  float z = 0.f;
-  if (m != kNegInf) {
-    for (int s = 0; s < ns; ++s) {
-      const int64_t part = part0 + (int64_t)s * a.h_q;
-      const float ls = a.ws_lse[part];
-      if (ls == kNegInf) continue;
-      const float wgt = __expf(ls - m);
+  for (int s0 = 0; s0 < ns; s0 += 4) {
+    float ls[4];
+    i32x4 pv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t part = part0 + (int64_t)min(s0 + j, ns - 1) * a.h_q;
+      ls[j] = a.ws_lse[part];
+      pv[j] = *(const i32x4*)(a.ws_o + part * kDv + 8 * q8);
+    }
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+      if (s0 + j >= ns) ls[j] = kNegInf;
+    const float mc = fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3]));
+    const float mn = fmaxf(m, mc);
+    if (mn == kNegInf) continue;                 // every part so far is empty
+    if (m != kNegInf && mn != m) {
+      const float r = __expf(m - mn);
+      z *= r;
+      acc0 *= r;
+      acc1 *= r;
+    }
+    m = mn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float wgt = ls[j] == kNegInf ? 0.f : __expf(ls[j] - m);
       z += wgt;
       // eight bf16 partial values -> fp32 (exact: bf16 is the top half of fp32)
-      const i32x4 pv = *(const i32x4*)(a.ws_o + part * kDv + 8 * q8);
       f32x4 lo4, hi4;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        lo4[2 * k] = __uint_as_float((uint32_t)pv[k] << 16);
-        lo4[2 * k + 1] = __uint_as_float((uint32_t)pv[k] & 0xFFFF0000u);
-        hi4[2 * k] = __uint_as_float((uint32_t)pv[k + 2] << 16);
-        hi4[2 * k + 1] = __uint_as_float((uint32_t)pv[k + 2] & 0xFFFF0000u);
+        lo4[2 * k] = __uint_as_float((uint32_t)pv[j][k] << 16);
+        lo4[2 * k + 1] = __uint_as_float((uint32_t)pv[j][k] & 0xFFFF0000u);
+        hi4[2 * k] = __uint_as_float((uint32_t)pv[j][k + 2] << 16);
+        hi4[2 * k + 1] = __uint_as_float((uint32_t)pv[j][k + 2] & 0xFFFF0000u);
       }
       acc0 += wgt * lo4;
       acc1 += wgt * hi4;
