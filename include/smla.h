@@ -135,8 +135,10 @@ typedef struct smla_fwd_params {
   /* tuning: 0 lets the planner choose.
    *   num_splits: parts of each token's topk range, each run by its own
    *               workgroup and merged by log-sum-exp (decode occupancy).
-   *   b_topk:     slots per block of the online softmax: 32 or 64 (bf16 KV),
- *               32 (fp8 KV). */
+   *   b_topk:     slots per block of the online softmax: 32, 64 or 128
+   *               (bf16 KV), 32 (fp8 and fp4 KV).  With bf16 KV a split of
+   *               at most 128 slots always runs as one block of 128 (all its
+   *               rows resident at once), whatever b_topk says. */
   int32_t num_splits;
   int32_t b_topk;
 
@@ -144,9 +146,10 @@ typedef struct smla_fwd_params {
    * 优化多核负载均衡: with causal or sparse masks tokens carry different
    * numbers of valid blocks, so tokens are dealt to the cores by valid-block
    * weight, not by count).
-   *   schedule: SMLA_SCHEDULE_AUTO (0) lets the planner choose (the grid: on
-   *             the measured workloads the hardware's own dispatch of one
-   *             workgroup per token balances as well, see the design notes);
+   *   schedule: SMLA_SCHEDULE_AUTO (0) lets the planner choose (the grid:
+   *             on prefill and causal prefill the hardware's own dispatch of
+   *             one workgroup per token balances as well as the weighted
+   *             runs, and pays no token-switch cost);
    *             SMLA_SCHEDULE_GRID (1): one workgroup per (token, split, group
    *             of 64 heads);
    *             SMLA_SCHEDULE_PERSISTENT (2): a fixed number of workgroups,

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsmla.so")
 # The forward kernels are split over several translation units (one per group
 # of launch configurations) so that they compile in parallel.
-SOURCES = ["smla_fwd_bf16_persist.hip", "smla_fwd_fp8_w4.hip", "smla_fwd_fp8_w1w2.hip", "smla_fwd_fp4.hip", "smla_fwd_bf16_w4_b32.hip",
+SOURCES = ["smla_fwd_bf16_persist.hip", "smla_fwd_bf16_b128.hip", "smla_fwd_fp8_w4.hip", "smla_fwd_fp8_w1w2.hip", "smla_fwd_fp4.hip", "smla_fwd_bf16_w4_b32.hip",
            "smla_fwd_bf16_w4_b64.hip", "smla_fwd_bf16_w1.hip", "smla_fwd_bf16_w2.hip",
            "smla_launch.hip", "smla_api.cpp"]
 ARCH = "gfx950"

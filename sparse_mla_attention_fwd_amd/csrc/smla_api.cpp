@@ -78,8 +78,8 @@ smla_status check_and_plan(const smla_fwd_params* p, Plan* plan) {
   if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_E4M3 &&
       p->kv_format != SMLA_KV_FP4_E2M1)
     return fail(SMLA_ERR_INVALID_ARGUMENT, "kv_format=%d unknown", p->kv_format);
-  if (p->b_topk != 0 && p->b_topk != 32 && p->b_topk != 64)
-    return fail(SMLA_ERR_UNSUPPORTED, "b_topk=%d: supported 32, 64 (0 = auto)", p->b_topk);
+  if (p->b_topk != 0 && p->b_topk != 32 && p->b_topk != 64 && p->b_topk != 128)
+    return fail(SMLA_ERR_UNSUPPORTED, "b_topk=%d: supported 32, 64, 128 (0 = auto)", p->b_topk);
   if (p->num_splits < 0) return fail(SMLA_ERR_INVALID_ARGUMENT, "num_splits=%d is negative", p->num_splits);
   if (p->schedule < SMLA_SCHEDULE_AUTO || p->schedule > SMLA_SCHEDULE_PERSISTENT)
     return fail(SMLA_ERR_INVALID_ARGUMENT, "schedule=%d unknown", p->schedule);

@@ -781,6 +781,218 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_short_kernel(FwdArgs a)
   });
 }
 
+// B_TOPK = 128 over a split of any length (page "Ascend Sparse Attention
+// Forward 算法与优化技术简析", section 计算流程 step 1 names 64 or 96 slots per
+// block; its section 讨论 argues for larger blocks when the per-block vector
+// work dominates): the block loop of the online softmax with blocks of 128
+// slots, one block resident in LDS as four 32-row stages.  QKᵀ runs stage by
+// stage as the rows arrive; one softmax step per 128 slots (running_max,
+// skip-scale rescale at RESCALE_THRES, running_sumexp); PV stage by stage,
+// and once every wave is done with a stage it is refilled with the next
+// block's rows (a barrier per stage), so the next block's gathers overlap the
+// rest of this block's PV.  One wave per 16 heads (h_q/16 waves, at most 64
+// heads per workgroup).
+template <int NW, bool SPLIT, bool BUF>
+__global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_b128_kernel(FwdArgs a) {
+  constexpr int BT = 32, NST = 4, BB = BT * NST;
+  constexpr int LPB = loads_per_block<NW, BT>();
+  constexpr int TILE = BT * kRowBytesBf16;
+  constexpr int NT = NW * 64;
+  constexpr int KT = BB / 16;                   // key tiles of 16 slots per block
+  constexpr int UNIT_GROUP = (BT / 8) * 1024;
+  __shared__ __attribute__((aligned(1024))) char st0[TILE];
+  __shared__ __attribute__((aligned(1024))) char st1[TILE];
+  __shared__ __attribute__((aligned(1024))) char st2[TILE];
+  __shared__ __attribute__((aligned(1024))) char st3[TILE];
+  __shared__ int sidx[kMaxSlotsPerSplit + BB];
+  __shared__ int swcnt[NW];
+  char* const stages[4] = {st0, st1, st2, st3};
+
+  WorkItem wi;
+  if (!work_item(a, wi)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int token = wi.token, split = wi.split;
+  const int lo = split * a.slots_per_split;
+  const int hi = min(a.topk, lo + a.slots_per_split);
+  const int head = wi.head0 + w * 16 + n;
+  const int nvalid = compact_slots<NW>(a.idx + (int64_t)token * a.idx_st, lo, hi, a.s_kv, sidx, swcnt, tid);
+  float* lsep;
+  uint16_t* row = out_row<SPLIT>(a, token, split, head, lsep);
+  if (nvalid == 0) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) *(i32x4*)(row + 32 * k + 8 * g) = i32x4{0, 0, 0, 0};
+    if (g == 0) *lsep = kNegInf;
+    return;
+  }
+  const int nblk = (nvalid + BB - 1) / BB;
+  // padding slots of the last block repeat the first valid row (weight 0)
+  for (int j = nvalid + tid; j < nblk * BB; j += NT) sidx[j] = sidx[0];
+  __syncthreads();
+
+  const LaneOffsets<BT> lofs = lane_offsets<BT>(lane);
+  const KvSource<BUF> src(a.kv, a.kv_window_bytes);
+  bf16x8 qf[18];
+  // block 0: stage 0's gathers, Q, stages 1..3 (loads complete in order)
+  static_for<0, NST>([&](auto B) __attribute__((always_inline)) {
+    constexpr int b = decltype(B)::value;
+    GatherPlan<NW, BT, BUF> gp;
+    gp.prepare(stages[b], src, a.kv_row_bytes, sidx + b * BT, tid);
+    gp.issue_all();
+    if constexpr (b == 0) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      load_q(a, token, head, g, qf);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  });
+
+  f32x4 o[32];
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) o[dt] = pin_agpr(f32x4{0.f, 0.f, 0.f, 0.f});
+  float running_max = kNegInf, running_max_for_softmax = kNegInf, sumexp = 0.f;
+  constexpr int PF = 12;
+  auto qk_off = [&](int i) __attribute__((always_inline)) {
+    const int s = i / 2, kt = i % 2;
+    return lofs.qk[s & 1] + (s >> 1) * UNIT_GROUP + kt * 2048;
+  };
+  auto tr_load = [&](const char* tile, int off) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS i16x4*)((LDS_AS char*)(LDS_AS void*)tile + off));
+  };
+  auto tr_off = [&](int dt) __attribute__((always_inline)) {
+    return lofs.tr[dt & 3] + (dt >> 2) * UNIT_GROUP;
+  };
+
+  for (int j = 0; j < nblk; ++j) {
+    // ---- Pᵀ = G·Qᵀ stage by stage (stage b: key tiles 2b, 2b+1)
+    f32x4 p[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) p[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    static_for<0, NST>([&](auto B) __attribute__((always_inline)) {
+      constexpr int b = decltype(B)::value;
+      const char* tile = stages[b];
+      wait_vm_lgkm0<(NST - 1 - b) * LPB>();
+      barrier_no_vm_drain();
+      f32x4 odd[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      bf16x8 abuf[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) abuf[i] = lds_load<bf16x8>(tile, qk_off(i));
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, 36>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value, s = i / 2, kt = i % 2;
+        if constexpr (s % 2 == 0)
+          p[2 * b + kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], p[2 * b + kt], 0, 0, 0);
+        else
+          odd[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[i % PF], qf[s], odd[kt], 0, 0, 0);
+        if constexpr (i + PF < 36) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      p[2 * b] += odd[0];
+      p[2 * b + 1] += odd[1];
+    });
+
+    // ---- online softmax step over the block's 128 slots
+    float x[KT][4];
+    float cur = kNegInf;
+    const int j0 = j * BB + 4 * g;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float val = p[kt][r] * a.scale_log2;
+        x[kt][r] = (j0 + 16 * kt + r < nvalid) ? val : kNegInf;
+        cur = fmaxf(cur, x[kt][r]);
+      }
+    cur = wave_max16x4(cur);
+    // every block holds a valid slot, so the new running max is finite
+    const float rmax = fmaxf(running_max, cur);
+    running_max = rmax;
+    if (__ballot(rmax - running_max_for_softmax > kRescaleThresLog2) != 0ull) {
+      if (running_max_for_softmax != kNegInf) {
+        const float alpha = __builtin_amdgcn_exp2f(running_max_for_softmax - rmax);
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) o[dt] = pin_agpr(pin_agpr(o[dt]) * alpha);
+        sumexp *= alpha;
+      }
+      running_max_for_softmax = rmax;
+    }
+    const float m = running_max_for_softmax;
+    bf16x8 sb[NST];
+#pragma unroll
+    for (int b = 0; b < NST; ++b) {
+      float sv[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[h][r] = __builtin_amdgcn_exp2f(x[2 * b + h][r] - m);
+          sumexp += sv[h][r];
+        }
+      union { uint32_t u[4]; bf16x8 v; } t;
+      t.u[0] = pack2_bf16(sv[0][0], sv[0][1]);
+      t.u[1] = pack2_bf16(sv[0][2], sv[0][3]);
+      t.u[2] = pack2_bf16(sv[1][0], sv[1][1]);
+      t.u[3] = pack2_bf16(sv[1][2], sv[1][3]);
+      sb[b] = t.v;
+    }
+
+    // ---- Oᵀ += Vᵀ·Sᵀ stage by stage; a stage is refilled with block j+1
+    // once every wave is past its products
+    const bool more = j + 1 < nblk;
+    static_for<0, NST>([&](auto B) __attribute__((always_inline)) {
+      constexpr int b = decltype(B)::value;
+      const char* tile = stages[b];
+      constexpr int PFV = 6;
+      i16x4 va[PFV], vb[PFV];
+#pragma unroll
+      for (int i = 0; i < PFV; ++i) {
+        va[i] = tr_load(tile, tr_off(i));
+        vb[i] = tr_load(tile, tr_off(i) + 2048);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, 32>([&](auto I) __attribute__((always_inline)) {
+        constexpr int dt = decltype(I)::value;
+        union { i16x4 h[2]; bf16x8 v; } av;
+        av.h[0] = va[dt % PFV];
+        av.h[1] = vb[dt % PFV];
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, sb[b], o[dt], 0, 0, 0);
+        if constexpr (dt + PFV < 32) {
+          va[dt % PFV] = tr_load(tile, tr_off(dt + PFV));
+          vb[dt % PFV] = tr_load(tile, tr_off(dt + PFV) + 2048);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (more) {
+        // every wave's reads of this stage have returned (its last products
+        // consumed them) before the barrier; then the refill may land
+        wait_vm_lgkm0<63>();
+        barrier_no_vm_drain();
+        GatherPlan<NW, BT, BUF> gp;
+        gp.prepare(stages[b], src, a.kv_row_bytes, sidx + (j + 1) * BB + b * BT, tid);
+        gp.issue_all();
+      }
+    });
+  }
+
+  // ---- epilogue: O / running_sumexp, 16-byte stores (rows 0<->1, 2<->3 of
+  // each tile pair swapped: 64 contiguous bytes per head)
+  const float l = wave_sum16x4(sumexp);
+  const float inv = 1.0f / l;
+  if (g == 0) *lsep = (running_max_for_softmax + __builtin_amdgcn_logf(l)) * kLn2;
+  uint16_t* base = row + ((g & 1) ? 16 + 4 * (g - 1) : 4 * g);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const f32x4 oe = pin_agpr(o[2 * k]), oo = pin_agpr(o[2 * k + 1]);
+    const uint32_t e0 = pack2_bf16(oe[0] * inv, oe[1] * inv), e1 = pack2_bf16(oe[2] * inv, oe[3] * inv);
+    const uint32_t o0 = pack2_bf16(oo[0] * inv, oo[1] * inv), o1 = pack2_bf16(oo[2] * inv, oo[3] * inv);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(e0, o0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(e1, o1, false, false);
+    *(i32x4*)(base + 32 * k) = i32x4{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+  }
+}
+
 template <int NW, int BT, int NST, bool SPLIT, bool BUF>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
   constexpr int LPB = loads_per_block<NW, BT>();
@@ -1008,9 +1220,9 @@ struct DequantRaw {
   float* stile;   // [5][BT] group-major copy of the block's scales
   int tid;
 
-  __device__ __forceinline__ void run(int k) {
+  __device__ __forceinline__ void run(int k, int t) {
     // Threads past the last task redo it: the same bytes written twice.
-    const int c = min(k * NT + tid, TASKS - 1);
+    const int c = min(k * NT + t, TASKS - 1);
     const int r = c / 36, cc = c - r * 36;
     // every task also copies one scale of its row (groups repeat: same value)
     const int gs = cc % 5;
@@ -1028,9 +1240,20 @@ struct DequantRaw {
           i32x4{(int)o[4 * h], (int)o[4 * h + 1], (int)o[4 * h + 2], (int)o[4 * h + 3]};
     }
   }
+  // Task k's addresses depend only on the thread and k, so left visible the
+  // compiler hoists every task's addresses out of the block loop; with one
+  // or two waves (18 or 9 tasks per thread) they no longer fit in registers.
+  // An opaque copy of the thread index keeps them local to each pass.
+  __device__ __forceinline__ int opaque_tid() const {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return t;
+  }
+  __device__ __forceinline__ void run(int k) { run(k, opaque_tid()); }
   __device__ __forceinline__ void run_all() {
+    const int t = opaque_tid();
 #pragma unroll
-    for (int k = 0; k < PER_THREAD; ++k) run(k);
+    for (int k = 0; k < PER_THREAD; ++k) run(k, t);
   }
 };
 
@@ -1141,23 +1364,28 @@ unsigned grid_size(const FwdArgs& a) {
   return (unsigned)(((int64_t)a.s_q + 7) / 8 * 8 * a.head_groups * a.num_splits);
 }
 
+// Short split (at most kShortSlots slots): one block of up to 128 slots, two
+// head groups per wave when inner_groups is 2.
+template <int NW, bool SPLIT, bool BUF>
+void launch_bf16_short(const FwdArgs& a, hipStream_t stream) {
+  const dim3 grid(grid_size(a)), block(NW * 64);
+  if constexpr (NW == 4) {
+    if (a.inner_groups == 2) {
+      hipLaunchKernelGGL((smla_fwd_bf16_short_kernel<NW, SPLIT, BUF, 2>), grid, block, 0, stream, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((smla_fwd_bf16_short_kernel<NW, SPLIT, BUF, 1>), grid, block, 0, stream, a);
+}
+
 template <int NW, int BT, bool SPLIT, bool BUF>
 void launch_bf16_variant(const FwdArgs& a, hipStream_t stream) {
   constexpr int NST = BT == 32 ? 4 : 2;
-  const dim3 grid(grid_size(a)), block(NW * 64);
-  if (a.slots_per_split <= kShortSlots) {
-    // short split: one block of up to 128 slots (two head groups per wave
-    // when inner_groups is 2)
-    if constexpr (NW == 4) {
-      if (a.inner_groups == 2) {
-        hipLaunchKernelGGL((smla_fwd_bf16_short_kernel<NW, SPLIT, BUF, 2>), grid, block, 0, stream, a);
-        return;
-      }
-    }
-    hipLaunchKernelGGL((smla_fwd_bf16_short_kernel<NW, SPLIT, BUF, 1>), grid, block, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, BUF>), grid, block, 0, stream, a);
-  }
+  if (a.slots_per_split <= kShortSlots)
+    launch_bf16_short<NW, SPLIT, BUF>(a, stream);
+  else
+    hipLaunchKernelGGL((smla_fwd_bf16_kernel<NW, BT, NST, SPLIT, BUF>), dim3(grid_size(a)), dim3(NW * 64), 0,
+                       stream, a);
 }
 
 template <int NW, bool SPLIT, bool BUF, class Fmt = KvFp8Format>

@@ -37,6 +37,30 @@ hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// bf16 KV, B_TOPK 128: short splits (at most 128 slots) in the one-block
+// kernel, longer ones in the 128-slot block loop.
+template <int NW>
+hipError_t launch_bf16_b128(const FwdArgs& a, hipStream_t stream) {
+  const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
+  if (a.slots_per_split <= kShortSlots) {
+    if (split)
+      buf ? launch_bf16_short<NW, true, true>(a, stream) : launch_bf16_short<NW, true, false>(a, stream);
+    else
+      buf ? launch_bf16_short<NW, false, true>(a, stream) : launch_bf16_short<NW, false, false>(a, stream);
+    return hipGetLastError();
+  }
+  const dim3 grid(grid_size(a)), block(NW * 64);
+  if (split && buf)
+    hipLaunchKernelGGL((smla_fwd_bf16_b128_kernel<NW, true, true>), grid, block, 0, stream, a);
+  else if (split)
+    hipLaunchKernelGGL((smla_fwd_bf16_b128_kernel<NW, true, false>), grid, block, 0, stream, a);
+  else if (buf)
+    hipLaunchKernelGGL((smla_fwd_bf16_b128_kernel<NW, false, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((smla_fwd_bf16_b128_kernel<NW, false, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int NW>
 hipError_t launch_fp4(const FwdArgs& a, hipStream_t stream) {
   const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;

@@ -91,6 +91,8 @@ hipError_t launch_bf16_persist(const FwdArgs& a, int grid, hipStream_t stream);
 template <int NW, int BT>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream);
 template <int NW>
+hipError_t launch_bf16_b128(const FwdArgs& a, hipStream_t stream);
+template <int NW>
 hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream);
 template <int NW>
 hipError_t launch_fp4(const FwdArgs& a, hipStream_t stream);

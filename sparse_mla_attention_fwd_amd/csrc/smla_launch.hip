@@ -167,6 +167,14 @@ hipError_t launch_fwd(const FwdArgs& a, int b_topk, int kv_format, hipStream_t s
       case 128: e = launch_fp8<4>(a, stream); break;   // 128: two head groups
       default: return hipErrorInvalidValue;
     }
+  } else if (b_topk == 128) {
+    switch (a.h_q) {
+      case 16: e = launch_bf16_b128<1>(a, stream); break;
+      case 32: e = launch_bf16_b128<2>(a, stream); break;
+      case 64:
+      case 128: e = launch_bf16_b128<4>(a, stream); break;   // 128: two head groups
+      default: return hipErrorInvalidValue;
+    }
   } else {
     switch (a.h_q) {
       case 16: e = b64 ? launch_bf16<1, 64>(a, stream) : launch_bf16<1, 32>(a, stream); break;

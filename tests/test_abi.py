@@ -161,6 +161,18 @@ def test_plans_of_named_workloads(name, splits):
     assert (w.topk + ns - 1) // ns <= cap
 
 
+def test_b_topk_128_is_a_bf16_block_size():
+    """B_TOPK 128 is accepted for bf16 KV (planned as asked, no block-count
+    workspace) and refused for the quantised formats."""
+    p = _params(topk=2048, indices_stride_token=2048, num_splits=1, b_topk=128)
+    assert _lib.smla_fwd_plan(p) == (1, 128)
+    assert _lib.smla_fwd_workspace_size(p) == 0
+    for fmt, row in ((1, 640), (2, 320)):
+        p = _params(kv_format=fmt, kv_stride_row=row, topk=1024, indices_stride_token=1024, b_topk=128)
+        with pytest.raises(_lib.SmlaError):
+            _lib.smla_fwd_plan(p)
+
+
 def test_topk_beyond_one_split_needs_more_parts():
     p = _params(topk=5000, indices_stride_token=5000, num_splits=2)
     with pytest.raises(_lib.SmlaError):

@@ -89,7 +89,7 @@ def test_tiny_workload_all_tokens(dev):
 
 
 @pytest.mark.parametrize("h_q", [16, 32, 64, 128])
-@pytest.mark.parametrize("b_topk", [32, 64])
+@pytest.mark.parametrize("b_topk", [32, 64, 128])
 def test_random_cases_heads_and_blocks(dev, h_q, b_topk):
     # topk 257: several blocks plus a ragged tail of one slot
     x = workloads.make_random(s_q=3, h_q=h_q, topk=257, s_kv=1000, seed=h_q + b_topk)
@@ -171,11 +171,51 @@ def test_deterministic(dev):
 
 def test_block_sizes_agree(dev):
     x = workloads.make_random(s_q=4, h_q=64, topk=1000, s_kv=8192, seed=12, q_mult=4.0)
-    a = run_gpu(dev, x, b_topk=32)
-    b = run_gpu(dev, x, b_topk=64)
     ro, rl = oracle_tokens(x)
-    check(*a, ro, rl, "B32")
-    check(*b, ro, rl, "B64")
+    for bt in (32, 64, 128):
+        check(*run_gpu(dev, x, b_topk=bt), ro, rl, f"B{bt}")
+
+
+# ---- B_TOPK 128: one online-softmax step per 128 slots (short splits: the
+# one-block kernel; longer splits: the 128-slot block loop)
+
+
+@pytest.mark.parametrize("h_q", [16, 64, 128])
+@pytest.mark.parametrize("topk,num_splits", [(300, 1), (1100, 1), (2048, 1), (2048, 2), (700, 6)])
+def test_b128_cases(dev, h_q, topk, num_splits):
+    """Ragged last blocks, masked and duplicate slots, Q x4 (rescales across
+    blocks), an empty token, leading and trailing blocks without a valid slot,
+    a token whose only valid slot is the last; rows no valid slot names are
+    NaN (a read of one would leak into the output)."""
+    x = workloads.make_random(s_q=6, h_q=h_q, topk=topk, s_kv=5000, seed=topk + h_q + num_splits + 128,
+                              invalid_frac=0.2, dup_frac=0.05, q_mult=4.0)
+    idx = x["indices"]
+    idx[1, :] = -1
+    idx[2, : topk // 2] = -1
+    idx[3, : topk - 1] = 10 ** 6
+    idx[4, 40:] = -1
+    used = np.zeros(5000, dtype=bool)
+    iv = idx.numpy()
+    used[iv[(iv >= 0) & (iv < 5000)]] = True
+    kv = x["kv"].clone()
+    kv[torch.from_numpy(~used)] = float("nan")
+    out, lse = run_gpu(dev, dict(x, kv=kv), num_splits=num_splits, b_topk=128)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"B128 h{h_q} topk={topk} splits={num_splits}")
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+def test_b128_all_slots_one_row_is_bit_exact(dev):
+    x = workloads.make_random(s_q=2, h_q=64, topk=2048, s_kv=500, seed=1281)
+    rows = [7, 499]
+    for t, r in enumerate(rows):
+        x["indices"][t, :] = r
+    out, lse = run_gpu(dev, x, b_topk=128, num_splits=1)
+    for t, r in enumerate(rows):
+        v = x["kv"][r, :512].float().numpy()
+        assert np.array_equal(out[t], np.broadcast_to(v, out[t].shape)), f"row {r} not exact"
+        xr = (workloads.to_f64(x["q"][t]) @ workloads.to_f64(x["kv"][r])) * x["sm_scale"]
+        assert np.abs(lse[t] - (xr + math.log(2048))).max() < 1e-4
 
 
 def test_strided_views(dev):
@@ -232,6 +272,10 @@ def test_prefill_full_size_all_tokens(dev):
 
 def test_causal_full_size_all_tokens(dev):
     _whole(dev, workloads.make_inputs("causal"))
+
+
+def test_prefill_full_size_all_tokens_b128(dev):
+    _whole(dev, workloads.make_inputs("prefill"), b_topk=128)
 
 
 @pytest.mark.parametrize("h_q", [16, 64])
