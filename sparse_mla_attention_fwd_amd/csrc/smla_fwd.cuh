@@ -1174,6 +1174,7 @@ struct RawGather {
   const int* sidx_blk;
   char* slot;
   int tid;
+  bool dummy = false;   // a block past the split: the same instructions, nothing useful loaded
 
   __device__ __forceinline__ void prepare(char* raw, const KvSource<BUF>& s, int64_t rb,
                                           const int* sb, int t) {
@@ -1183,16 +1184,26 @@ struct RawGather {
     sidx_blk = sb;
     tid = t;
   }
+  // Loads past the end of the split: buffer loads at the out-of-window offset
+  // (dropped by the range check), 64-bit loads of row 0 (inside the KV).
+  __device__ __forceinline__ void prepare_dummy(char* raw, const KvSource<BUF>& s, int t) {
+    slot = raw;
+    src = s;
+    row_bytes = 0;
+    sidx_blk = nullptr;
+    tid = t;
+    dummy = true;
+  }
   __device__ __forceinline__ void issue(int k) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     int u = k * NW + w;                                    // wave-uniform
     if (UNITS % NW != 0 && u >= UNITS) u -= NW;            // repeat this wave's previous unit
     const int c = u * 64 + l;
     const int row = c / CHUNKS, ch = c - row * CHUNKS;
-    const int kvrow = sidx_blk[row];
+    const int kvrow = dummy ? 0 : sidx_blk[row];
     if constexpr (BUF)
-      src.load16((LDS_AS void*)(slot + u * 1024), (uint32_t)kvrow * (uint32_t)row_bytes + (ch << 4),
-                 nullptr, 0);
+      src.load16((LDS_AS void*)(slot + u * 1024),
+                 dummy ? kDummyOffset : (uint32_t)kvrow * (uint32_t)row_bytes + (ch << 4), nullptr, 0);
     else
       src.load16((LDS_AS void*)(slot + u * 1024), 0, src.kv + (int64_t)kvrow * row_bytes + (ch << 4), 0);
   }

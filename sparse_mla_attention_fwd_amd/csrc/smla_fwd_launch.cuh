@@ -3,6 +3,7 @@
 #pragma once
 
 #include "smla_fwd_fp8_pipe.cuh"
+#include "smla_fwd_q_pipe.cuh"
 
 namespace smla {
 
@@ -64,6 +65,20 @@ hipError_t launch_bf16_b128(const FwdArgs& a, hipStream_t stream) {
 template <int NW>
 hipError_t launch_fp4(const FwdArgs& a, hipStream_t stream) {
   const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
+  if constexpr (NW == 4) {
+    // 64 heads per workgroup: the pipelined kernel with one conversion per
+    // block and workgroup
+    const dim3 grid(grid_size(a)), block(256);
+    if (split && buf)
+      hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<true, true, KvFp4Format>), grid, block, 0, stream, a);
+    else if (split)
+      hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<true, false, KvFp4Format>), grid, block, 0, stream, a);
+    else if (buf)
+      hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<false, true, KvFp4Format>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<false, false, KvFp4Format>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   if (split)
     buf ? launch_fp8_variant<NW, true, true, KvFp4Format>(a, stream)
         : launch_fp8_variant<NW, true, false, KvFp4Format>(a, stream);
