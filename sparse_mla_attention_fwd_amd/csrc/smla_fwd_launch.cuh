@@ -2,13 +2,9 @@
 // smla_fwd_*.hip units).
 #pragma once
 
-#include "smla_fwd_fp8_pipe.cuh"
 #include "smla_fwd_q_pipe.cuh"
 
 namespace smla {
-
-// Raw-row stages of the pipelined fp8 kernel.
-constexpr int kFp8Stages = 6;
 
 template <int NW, int BT>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
@@ -78,37 +74,40 @@ hipError_t launch_fp4(const FwdArgs& a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<false, false, KvFp4Format>), grid, block, 0, stream, a);
     return hipGetLastError();
+  } else {
+    if (split)
+      buf ? launch_fp8_variant<NW, true, true, KvFp4Format>(a, stream)
+          : launch_fp8_variant<NW, true, false, KvFp4Format>(a, stream);
+    else
+      buf ? launch_fp8_variant<NW, false, true, KvFp4Format>(a, stream)
+          : launch_fp8_variant<NW, false, false, KvFp4Format>(a, stream);
+    return hipGetLastError();
   }
-  if (split)
-    buf ? launch_fp8_variant<NW, true, true, KvFp4Format>(a, stream)
-        : launch_fp8_variant<NW, true, false, KvFp4Format>(a, stream);
-  else
-    buf ? launch_fp8_variant<NW, false, true, KvFp4Format>(a, stream)
-        : launch_fp8_variant<NW, false, false, KvFp4Format>(a, stream);
-  return hipGetLastError();
 }
 
 template <int NW>
 hipError_t launch_fp8(const FwdArgs& a, hipStream_t stream) {
   const bool split = a.num_splits > 1, buf = a.kv_window_bytes != 0;
   if constexpr (NW == 4) {
-    // 64 heads per workgroup: the pipelined kernel with in-register conversion
+    // 64 heads per workgroup: the pipelined kernel with one conversion per
+    // block and workgroup
     const dim3 grid(grid_size(a)), block(256);
     if (split && buf)
-      hipLaunchKernelGGL((smla_fwd_fp8_pipe_kernel<true, true, kFp8Stages>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<true, true, KvFp8Format>), grid, block, 0, stream, a);
     else if (split)
-      hipLaunchKernelGGL((smla_fwd_fp8_pipe_kernel<true, false, kFp8Stages>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<true, false, KvFp8Format>), grid, block, 0, stream, a);
     else if (buf)
-      hipLaunchKernelGGL((smla_fwd_fp8_pipe_kernel<false, true, kFp8Stages>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<false, true, KvFp8Format>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((smla_fwd_fp8_pipe_kernel<false, false, kFp8Stages>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((smla_fwd_q_pipe_kernel<false, false, KvFp8Format>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  } else {
+    if (split)
+      buf ? launch_fp8_variant<NW, true, true>(a, stream) : launch_fp8_variant<NW, true, false>(a, stream);
+    else
+      buf ? launch_fp8_variant<NW, false, true>(a, stream) : launch_fp8_variant<NW, false, false>(a, stream);
     return hipGetLastError();
   }
-  if (split)
-    buf ? launch_fp8_variant<NW, true, true>(a, stream) : launch_fp8_variant<NW, true, false>(a, stream);
-  else
-    buf ? launch_fp8_variant<NW, false, true>(a, stream) : launch_fp8_variant<NW, false, false>(a, stream);
-  return hipGetLastError();
 }
 
 }  // namespace smla

@@ -1,6 +1,5 @@
-// Software-pipelined forward kernel for a quantised KV cache whose raw rows are
-// small enough to leave room for bf16 stages (fp4 E2M1: 320-byte rows), 64
-// heads per workgroup, B_TOPK 32.
+// Software-pipelined forward kernel for a quantised KV cache (fp8 E4M3 rows of
+// 640 bytes, fp4 E2M1 rows of 320), 64 heads per workgroup, B_TOPK 32.
 //
 // Method as in smla_fwd.cuh (page "Ascend Sparse Attention Forward
 // 算法与优化技术简析", sections 数学建模 and 计算流程); the KV rows are the packed
@@ -13,9 +12,10 @@
 // Each block's codes are converted ONCE per workgroup, into a bf16 stage in the
 // layout of the bf16 kernels, and the products then run as in the bf16
 // pipelined kernel (smla_fwd_pipe.cuh: d_v split of PV, QKᵀ of block i+1 before
-// PV of block i, softmax of block i+1 between the PV MFMAs).  Converting in
-// registers instead (the fp8 pipelined kernel) repeats the conversion of every
-// K code in each of the four waves.  Per iteration i:
+// PV of block i, softmax of block i+1 between the PV MFMAs).  Converting the
+// codes in registers at the operand reads instead repeats the conversion of
+// every K code in each of the four waves.  Raw stages: four for fp4, two for
+// fp8 (what fits beside two bf16 stages and the S exchange).  Per iteration i:
 //   barrier; QKᵀ(i+1) on bf16 stage (i+1)&1 and PV(i) on stage i&1, the raw
 //   stage freed in the last iteration refilled with block i+1+NR by gathers
 //   spread over the MFMAs;
@@ -37,7 +37,10 @@ namespace {
 template <bool SPLIT, bool BUF, class Fmt>
 __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
   constexpr int NW = 4, BT = 32, KT = 2;
-  constexpr int NR = 4;                       // raw stages: blocks in flight ahead of the conversion
+  constexpr bool FP4 = Fmt::ROW == 320;
+  // raw stages: blocks in flight ahead of the conversion (what fits beside two
+  // bf16 stages and the S exchange)
+  constexpr int NR = FP4 ? 4 : 2;
   constexpr int NQ = 36;                      // QK MFMAs per block
   constexpr int NPV = 32;                     // PV MFMAs per block
   using Gather = RawGather<NW, BUF, Fmt>;
@@ -48,12 +51,12 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
   constexpr int PF = 12;                      // K operand reads in flight
   constexpr int PFV = 4;                      // V fragments (two reads each) in flight
   constexpr int XS = NW * NW * 64 * 16;       // S operands of one block: [V group][head tile][lane]
-  static_assert(NR == 4, "the iteration loop is unrolled by four");
+  static_assert(4 % NR == 0, "the iteration loop is unrolled by four");
   static_assert(NR * RAW + 2 * TILE + 2 * XS + Fmt::MAX_SLOTS * 4 < 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) char rw0[RAW];
   __shared__ __attribute__((aligned(1024))) char rw1[RAW];
-  __shared__ __attribute__((aligned(1024))) char rw2[RAW];
-  __shared__ __attribute__((aligned(1024))) char rw3[RAW];
+  __shared__ __attribute__((aligned(1024))) char rw2[NR > 2 ? RAW : 16];
+  __shared__ __attribute__((aligned(1024))) char rw3[NR > 3 ? RAW : 16];
   __shared__ __attribute__((aligned(1024))) char tl0[TILE];
   __shared__ __attribute__((aligned(1024))) char tl1[TILE];
   __shared__ __attribute__((aligned(16))) float sc0[5 * BT];
@@ -106,45 +109,70 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
     };
     // Convert raw stage R into bf16 stage / scale tile p.  Wave w converts row
     // block w: lane l takes row 8w + l%8 and the 16-byte bf16 chunks
-    // 8k + l/8, k < 9 (8 codes = 4 raw bytes each, exact at scale 1), and
+    // 8k + l/8, k < 9 (8 codes: 4 raw bytes of E2M1 or 8 of E4M3, exact at
+    // scale 1), and
     // writes chunk k to slot l of unit (k, w) of the stage: every store of the
     // wave is one contiguous 1 KB unit (no bank conflict).  Lanes 0..39 also
     // copy scale group l/8 of their row.  The raw reads are one asm block that
     // waits for its own results: the caller's wait and barrier guarantee the
     // rows have landed, and reads the compiler could see would make it wait
     // for every younger gather as well.
-    static_assert(Fmt::ROW == 320 && Fmt::CODE_BYTES == 288, "E2M1 rows: two codes per byte");
+    static_assert(FP4 ? Fmt::CODE_BYTES == 288 : (Fmt::ROW == 640 && Fmt::CODE_BYTES == 576), "row formats");
     auto convert = [&](auto R, int p) __attribute__((always_inline)) {
       constexpr int r = decltype(R)::value;
       const int row = 8 * w + (lane & 7), gsel = min(lane >> 3, 4);
       const uint32_t rbase = (uint32_t)(uintptr_t)(const LDS_AS void*)raws[r] + row * Fmt::ROW;
-      const uint32_t caddr = rbase + (lane >> 3) * 4, saddr = rbase + Fmt::CODE_BYTES + gsel * 4;
-      uint32_t code[9];
+      // 8 codes per chunk: 4 bytes (E2M1) or 8 bytes (E4M3)
+      const uint32_t caddr = rbase + (lane >> 3) * (FP4 ? 4 : 8), saddr = rbase + Fmt::CODE_BYTES + gsel * 4;
       float scl;
-      asm volatile(
-          "ds_read_b32 %0, %10\n\tds_read_b32 %1, %10 offset:32\n\tds_read_b32 %2, %10 offset:64\n\t"
-          "ds_read_b32 %3, %10 offset:96\n\tds_read_b32 %4, %10 offset:128\n\tds_read_b32 %5, %10 offset:160\n\t"
-          "ds_read_b32 %6, %10 offset:192\n\tds_read_b32 %7, %10 offset:224\n\tds_read_b32 %8, %10 offset:256\n\t"
-          "ds_read_b32 %9, %11\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          // early-clobber: a read's result must not land in a register that
-          // still holds an address of the block
-          : "=&v"(code[0]), "=&v"(code[1]), "=&v"(code[2]), "=&v"(code[3]), "=&v"(code[4]),
-            "=&v"(code[5]), "=&v"(code[6]), "=&v"(code[7]), "=&v"(code[8]), "=&v"(scl)
-          : "v"(caddr), "v"(saddr)
-          : "memory");
+      uint32_t o[9][4];
+      if constexpr (FP4) {
+        uint32_t code[9];
+        asm volatile(
+            "ds_read_b32 %0, %10\n\tds_read_b32 %1, %10 offset:32\n\tds_read_b32 %2, %10 offset:64\n\t"
+            "ds_read_b32 %3, %10 offset:96\n\tds_read_b32 %4, %10 offset:128\n\tds_read_b32 %5, %10 offset:160\n\t"
+            "ds_read_b32 %6, %10 offset:192\n\tds_read_b32 %7, %10 offset:224\n\tds_read_b32 %8, %10 offset:256\n\t"
+            "ds_read_b32 %9, %11\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            // early-clobber: a read's result must not land in a register that
+            // still holds an address of the block
+            : "=&v"(code[0]), "=&v"(code[1]), "=&v"(code[2]), "=&v"(code[3]), "=&v"(code[4]),
+              "=&v"(code[5]), "=&v"(code[6]), "=&v"(code[7]), "=&v"(code[8]), "=&v"(scl)
+            : "v"(caddr), "v"(saddr)
+            : "memory");
+#pragma unroll
+        for (int k = 0; k < 9; ++k)
+          static_for<0, 4>([&](auto J) __attribute__((always_inline)) {
+            // byte j: columns 8c + 2j (low nibble) and 8c + 2j + 1 (high nibble)
+            constexpr int j = decltype(J)::value;
+            o[k][j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(code[k], 1.0f, j));
+          });
+      } else {
+        i32x2 code[9];
+        asm volatile(
+            "ds_read_b64 %0, %10\n\tds_read_b64 %1, %10 offset:64\n\tds_read_b64 %2, %10 offset:128\n\t"
+            "ds_read_b64 %3, %10 offset:192\n\tds_read_b64 %4, %10 offset:256\n\tds_read_b64 %5, %10 offset:320\n\t"
+            "ds_read_b64 %6, %10 offset:384\n\tds_read_b64 %7, %10 offset:448\n\tds_read_b64 %8, %10 offset:512\n\t"
+            "ds_read_b32 %9, %11\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(code[0]), "=&v"(code[1]), "=&v"(code[2]), "=&v"(code[3]), "=&v"(code[4]),
+              "=&v"(code[5]), "=&v"(code[6]), "=&v"(code[7]), "=&v"(code[8]), "=&v"(scl)
+            : "v"(caddr), "v"(saddr)
+            : "memory");
+#pragma unroll
+        for (int k = 0; k < 9; ++k)
+          static_for<0, 4>([&](auto J) __attribute__((always_inline)) {
+            // word j/2, half j%2: columns 8c + 2j and 8c + 2j + 1
+            constexpr int j = decltype(J)::value;
+            o[k][j] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)code[k][j >> 1], 1.0f, (j & 1) != 0));
+          });
+      }
       if (lane < 40) stiles[p][gsel * BT + row] = scl;
 #pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        uint32_t o[4];
-        static_for<0, 4>([&](auto J) __attribute__((always_inline)) {
-          // byte j: columns 8c + 2j (low nibble) and 8c + 2j + 1 (high nibble)
-          constexpr int j = decltype(J)::value;
-          o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(code[k], 1.0f, j));
-        });
+      for (int k = 0; k < 9; ++k)
         *(LDS_AS i32x4*)((LDS_AS char*)(LDS_AS void*)tiles[p] + (k * 4 + w) * 1024 + lane * 16) =
-            i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-      }
+            i32x4{(int)o[k][0], (int)o[k][1], (int)o[k][2], (int)o[k][3]};
     };
 
     bf16x8 qf[18];
@@ -244,7 +272,7 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
       float cur, alpha;
       bool any;
     };
-    auto soft_step = [&](auto K, Soft& sm, const QkOut& qo, int j0, const f32x4 (&sc4)[KT][4], int p)
+    auto soft_step = [&](auto K, Soft& sm, const QkOut& qo, int j0, const f32x4 (&sc4)[NW][KT], int p)
         __attribute__((always_inline)) {
 #pragma clang fp contract(off)
       constexpr int k = decltype(K)::value;
@@ -290,31 +318,30 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
 #pragma unroll
         for (int G = 0; G < NW; ++G) {
           union { uint32_t u[4]; bf16x8 v; } t;
-          t.u[0] = pack2_bf16(sm.x[0][0] * sc4[0][0][G], sm.x[0][1] * sc4[0][1][G]);
-          t.u[1] = pack2_bf16(sm.x[0][2] * sc4[0][2][G], sm.x[0][3] * sc4[0][3][G]);
-          t.u[2] = pack2_bf16(sm.x[1][0] * sc4[1][0][G], sm.x[1][1] * sc4[1][1][G]);
-          t.u[3] = pack2_bf16(sm.x[1][2] * sc4[1][2][G], sm.x[1][3] * sc4[1][3][G]);
+          t.u[0] = pack2_bf16(sm.x[0][0] * sc4[G][0][0], sm.x[0][1] * sc4[G][0][1]);
+          t.u[1] = pack2_bf16(sm.x[0][2] * sc4[G][0][2], sm.x[0][3] * sc4[G][0][3]);
+          t.u[2] = pack2_bf16(sm.x[1][0] * sc4[G][1][0], sm.x[1][1] * sc4[G][1][1]);
+          t.u[3] = pack2_bf16(sm.x[1][2] * sc4[G][1][2], sm.x[1][3] * sc4[G][1][3]);
           *(LDS_AS bf16x8*)((LDS_AS char*)(LDS_AS void*)xss[p] + ((G * NW + w) * 64 + lane) * 16) = t.v;
         }
         *(LDS_AS float*)((LDS_AS char*)(LDS_AS void*)xas[p] + (w * 16 + n) * 4) = sm.alpha;   // same in all g
       }
     };
     constexpr int NSOFT = 6;
-    // V-group scales (groups 0..3) of this lane's keys 16kt + 4g + r
-    auto read_scales = [&](const float* stile, f32x4 (&sc4)[KT][4]) __attribute__((always_inline)) {
+    // V-group scales (groups 0..3) of this lane's keys 16kt + 4g + r: sc4[G][kt][r]
+    // (one 16-byte read per group and key tile: the tile is group-major)
+    auto read_scales = [&](const float* stile, f32x4 (&sc4)[NW][KT]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+      for (int G = 0; G < NW; ++G)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sc4[kt][r] = f32x4{stile[0 * BT + 16 * kt + 4 * g + r], stile[1 * BT + 16 * kt + 4 * g + r],
-                             stile[2 * BT + 16 * kt + 4 * g + r], stile[3 * BT + 16 * kt + 4 * g + r]};
+        for (int kt = 0; kt < KT; ++kt) sc4[G][kt] = lds_load<f32x4>((const char*)stile, (G * BT + 16 * kt + 4 * g) * 4);
     };
 
     // block 0: QKᵀ and softmax, published for iteration 0
     {
       QkOut qo;
       qk(tiles[0], stiles[0], qo, [&](auto) {});
-      f32x4 sc4[KT][4];
+      f32x4 sc4[NW][KT];
       read_scales(stiles[0], sc4);
       Soft sm;
       static_for<0, NSOFT>([&](auto K) __attribute__((always_inline)) {
@@ -361,7 +388,7 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
       };
 
       QkOut qo;
-      f32x4 sc4[KT][4];
+      f32x4 sc4[NW][KT];
       if (next) {
         qk(tiles[p ^ 1], stiles[p ^ 1], qo, [&](auto I) __attribute__((always_inline)) {
           constexpr int q = decltype(I)::value;

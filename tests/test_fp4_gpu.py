@@ -106,3 +106,29 @@ def test_decode_fp4_full_size_all_tokens(dev):
     out, lse = run_fp4(dev, x, num_splits=x["workload"].num_splits)
     ro, rl = oracle_fp4(x)
     check_whole_config(out, lse, ro, rl, "decode_fp4 all tokens")
+
+
+@pytest.mark.parametrize("h_q", [64, 128])
+@pytest.mark.parametrize("topk,num_splits", [(1100, 1), (2048, 2), (2048, 3), (40, 1)])
+def test_fp4_long_splits_pipelined(dev, h_q, topk, num_splits):
+    """The 64-head fp4 kernel over many blocks (its raw-stage ring wraps
+    around several times): ragged last blocks, masked and repeated slots, Q x 4
+    (rescales across blocks), an empty token, leading and trailing slots
+    without a valid index, a token whose only valid slot is the last.  Rows no
+    valid slot names get NaN scales: a read of one would leak into the output."""
+    x = workloads.make_random(s_q=6, h_q=h_q, topk=topk, s_kv=5000, seed=topk + h_q + num_splits + 4,
+                              kv_format="fp4", invalid_frac=0.2, dup_frac=0.05, q_mult=4.0)
+    idx = x["indices"]
+    idx[1, :] = -1
+    idx[2, : topk // 2] = -1
+    idx[3, : topk - 1] = 10 ** 6
+    idx[4, 20:] = -1
+    iv = idx.numpy()
+    used = np.zeros(5000, dtype=bool)
+    used[iv[(iv >= 0) & (iv < 5000)]] = True
+    scales = x["kv_scales"].clone()
+    scales[torch.from_numpy(~used)] = float("nan")
+    out, lse = run_fp4(dev, dict(x, kv_scales=scales), num_splits=num_splits)
+    ro, rl = oracle_fp4(x)
+    check(out, lse, ro, rl, f"fp4 long h{h_q} topk={topk} splits={num_splits}")
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
