@@ -6,6 +6,7 @@ stream.  There is no fallback: if the library is missing the import fails.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -13,6 +14,8 @@ import torch  # noqa: F401  (loads the process's HIP runtime before libsmla bind
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsmla.so")
+# The LDS-poisoning debug build (same ABI; tests of races and unwritten LDS)
+POISON_LIB_PATH = os.path.join(HERE, "libsmla_poison.so")
 
 SMLA_OK = 0
 SMLA_ERR_INVALID_ARGUMENT = 1
@@ -119,6 +122,20 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"libsmla ABI version {lib.smla_abi_version()} != {ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Inside the block every call of this binding goes to the library at
+    ``path`` (another build of the same ABI, such as POISON_LIB_PATH); the
+    library loaded before is restored afterwards."""
+    global _lib
+    saved = _lib
+    _lib = None
+    try:
+        yield load(path)
+    finally:
+        _lib = saved
 
 
 def status_string(status: int) -> str:

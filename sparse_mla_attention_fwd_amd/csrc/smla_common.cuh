@@ -68,6 +68,40 @@ __device__ __forceinline__ int lds_read_opaque(const char* p) {
   return v;
 }
 
+// LDS-poisoning debug build (SMLA_DEBUG_LDS_POISON): races between the waves
+// of a workgroup and reads of LDS that nothing has written show up as NaN in
+// the results instead of as plausible stale values.  All-ones bytes read as
+// NaN in bf16, fp32 and the E4M3 codes, and as -1 (an invalid, masked slot,
+// never an address) in the index arrays.
+//  * debug_poison_lds(): every byte of the kernel's static LDS, at entry.
+//  * debug_poison_dma<B>(lds): the B bytes (16 or 4) a direct-to-LDS load of
+//    this lane will write, just before the load is issued, so that a read that
+//    is not ordered after the load's completion sees poison, not the previous
+//    block.
+// Both are empty in the product build.
+__device__ __forceinline__ void debug_poison_lds() {
+#ifdef SMLA_DEBUG_LDS_POISON
+  const uint32_t size = __builtin_amdgcn_groupstaticsize();
+  for (uint32_t off = threadIdx.x * 4; off + 4 <= size; off += blockDim.x * 4)
+    asm volatile("ds_write_b32 %0, %1" : : "v"(off), "v"(-1) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __syncthreads();
+#endif
+}
+template <int B = 16>
+__device__ __forceinline__ void debug_poison_dma(LDS_AS void* lds) {
+  static_assert(B == 16 || B == 4, "direct-to-LDS load sizes in use");
+#ifdef SMLA_DEBUG_LDS_POISON
+  const uint32_t addr = (uint32_t)(uintptr_t)lds + __lane_id() * B;
+  if constexpr (B == 16)
+    asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(i32x4{-1, -1, -1, -1}) : "memory");
+  else
+    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(-1) : "memory");
+#else
+  (void)lds;
+#endif
+}
+
 // s_waitcnt with vmcnt = vm (clamped to the 6-bit field) and lgkmcnt = 0.
 template <int VM>
 __device__ __forceinline__ void wait_vm_lgkm0() {

@@ -94,6 +94,7 @@ struct KvSource {
   // into lds + 16·lane.
   __device__ __forceinline__ void load16(LDS_AS void* lds, uint32_t voff, const char* vaddr,
                                          int add) const {
+    debug_poison_dma(lds);
     if constexpr (BUF)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, voff, add, 0, 0);
     else
@@ -553,6 +554,7 @@ __device__ __forceinline__ uint16_t* out_row(const FwdArgs& a, int token, int sp
 //     output accumulators (AGPRs) in PV only.
 template <int NW, bool SPLIT, bool BUF, int NG>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_short_kernel(FwdArgs a) {
+  debug_poison_lds();
   constexpr int BT = 32, NST = 4, MAXS = BT * NST;
   constexpr int LPB = loads_per_block<NW, BT>();
   constexpr int TILE = BT * kRowBytesBf16;
@@ -794,6 +796,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_short_kernel(FwdArgs a)
 // heads per workgroup).
 template <int NW, bool SPLIT, bool BUF>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_b128_kernel(FwdArgs a) {
+  debug_poison_lds();
   constexpr int BT = 32, NST = 4, BB = BT * NST;
   constexpr int LPB = loads_per_block<NW, BT>();
   constexpr int TILE = BT * kRowBytesBf16;
@@ -995,6 +998,7 @@ __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_b128_kernel(FwdArgs a) 
 
 template <int NW, int BT, int NST, bool SPLIT, bool BUF>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_bf16_kernel(FwdArgs a) {
+  debug_poison_lds();
   constexpr int LPB = loads_per_block<NW, BT>();
   constexpr int TILE = BT * kRowBytesBf16;
   // Statically distinct stage buffers: the compiler tracks direct-to-LDS
@@ -1270,6 +1274,7 @@ struct DequantRaw {
 
 template <int NW, bool SPLIT, bool BUF, class Fmt = KvFp8Format>
 __global__ __launch_bounds__(NW * 64) void smla_fwd_fp8_kernel(FwdArgs a) {
+  debug_poison_lds();
   constexpr int BT = 32;
   constexpr int NSTR = 4;                                  // raw ring depth
   constexpr int LPB = RawGather<NW, BUF, Fmt>::PER_WAVE;

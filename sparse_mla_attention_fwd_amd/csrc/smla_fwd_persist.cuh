@@ -60,6 +60,7 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 template <int DUMMY>
 __global__ __launch_bounds__(256) void smla_fwd_bf16_persist_kernel(FwdArgs a, const int32_t* __restrict__ nbp) {
+  debug_poison_lds();
   constexpr int NW = 4, BT = 32, KT = 2;
   constexpr int NQ = 36;                      // QK MFMAs per block
   constexpr int NPV = 32;                     // PV MFMAs per block
@@ -193,6 +194,7 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_persist_kernel(FwdArgs a, c
     const __amdgpu_buffer_rsrc_t irs =
         __builtin_amdgcn_make_buffer_rsrc((void*)irow, 0, in ? topk * 4 : 0, 0x00020000);
     const int j = c.b * BT + 8 * w + (lane & 7);
+    debug_poison_dma<4>((LDS_AS void*)(&ring[decltype(R)::value][w * 64]));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, (LDS_AS void*)(&ring[decltype(R)::value][w * 64]), 4,
                                              (uint32_t)j * 4u, 0, 0, 0);
   };

@@ -131,6 +131,7 @@ struct PipeState {
 // for the ring indices only (issued ahead of Q), not for Q or a scan.
 template <bool SPLIT, bool BUF, bool PRE = false>
 __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
+  debug_poison_lds();
   static_assert(!PRE || (BUF && !SPLIT), "precomputed block counts: one split, 32-bit window");
   constexpr int NW = 4, BT = 32, KT = 2;
   constexpr int NQ = 36;                      // QK MFMAs per block
@@ -198,6 +199,7 @@ __global__ __launch_bounds__(256) void smla_fwd_bf16_pipe_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc((void*)irow, 0, hi * 4, 0x00020000);
   auto load_idx = [&](int b, auto R) __attribute__((always_inline)) {
     const int j = lo + b * BT + 8 * w + (lane & 7);
+    debug_poison_dma<4>((LDS_AS void*)(&ring[decltype(R)::value][w * 64]));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, (LDS_AS void*)(&ring[decltype(R)::value][w * 64]), 4,
                                              (uint32_t)j * 4u, 0, 0, 0);
   };

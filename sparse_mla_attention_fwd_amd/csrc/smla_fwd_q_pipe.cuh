@@ -36,6 +36,7 @@ namespace {
 
 template <bool SPLIT, bool BUF, class Fmt>
 __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
+  debug_poison_lds();
   constexpr int NW = 4, BT = 32, KT = 2;
   constexpr bool FP4 = Fmt::ROW == 320;
   // raw stages: blocks in flight ahead of the conversion (what fits beside two

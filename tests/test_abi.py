@@ -358,3 +358,16 @@ def test_schedule_planning():
         p = _params(**{field: value})
         with pytest.raises(_lib.SmlaError):
             _lib.smla_fwd_plan(p)
+
+
+def test_poison_debug_library_loads_with_the_same_exports():
+    """The LDS-poisoning debug build (tests/test_lds_poison_gpu.py) exports the
+    same ABI, and switching the binding to it restores the product library."""
+    before = _lib.load()
+    with _lib.library(_lib.POISON_LIB_PATH) as dbg:
+        assert dbg is not before
+        for name in _declared_functions():
+            assert hasattr(dbg, name), name
+        assert dbg.smla_abi_version() == _lib.ABI_VERSION
+        assert _lib.load() is dbg
+    assert _lib.load() is before
