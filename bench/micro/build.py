@@ -1,10 +1,11 @@
-"""Build the two measurement programs of this folder for gfx950.
+"""Build the measurement programs of this folder for gfx950.
 
-    python bench/micro/build.py        # -> bench/micro/gather_ceiling, bench/micro/issue_probe
+    python bench/micro/build.py        # -> bench/micro/gather_ceiling, issue_probe, lds_patterns
 
 They are standalone HIP programs (they allocate their own buffers) that
 measure the hardware limits behind the forward kernels' design: the random-row
-gather ceiling of the memory system and the issue rate of one wave's MFMAs.
+gather ceiling of the memory system, the issue rate of one wave's MFMAs and the
+LDS cost of the operand-read patterns of two stage layouts.
 They are not part of the library and are not built with it.
 """
 from __future__ import annotations
@@ -15,7 +16,7 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PROGRAMS = ("gather_ceiling", "issue_probe")
+PROGRAMS = ("gather_ceiling", "issue_probe", "lds_patterns")
 
 
 def hipcc() -> str:

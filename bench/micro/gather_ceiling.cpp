@@ -12,7 +12,10 @@
 //   lines:  eight random rows x one 128-byte line (the bf16 kernels' shape);
 //   rows:   64 consecutive 16-byte chunks of the wave's eight rows laid end to
 //           end, i.e. 1 KB of one or two rows (the raw-row shape of the
-//           quantised kernels).
+//           quantised kernels);
+//   quads:  four rows x 256 bytes, and pairs: two rows x 512 bytes (1152-byte
+//           rows only: eight such instructions cover the first 1 KB of the
+//           group's eight rows, a ninth the last line of all eight).
 // Loads: direct-to-LDS (what the kernels use) with D instructions in flight
 // per wave, 4/8/16 waves per workgroup, one or two workgroups per CU; and
 // plain loads into registers.  Every address lies inside the buffer: row =
@@ -58,6 +61,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 // MODE 0: direct-to-LDS 16-byte loads, at most D in flight per wave, lines shape.
 // MODE 1: 16-byte loads into registers in batches of D, lines shape.
 // MODE 2: direct-to-LDS 16-byte loads, at most D in flight per wave, rows shape.
+// MODE 3 / 4: as MODE 0 in the quads / pairs shape.
 template <int MODE, int D>
 __global__ void gather_kernel(const char* __restrict__ kv, uint32_t rows_per_slice, uint32_t nslices,
                               int row_bytes, int groups_per_wave, uint32_t* sink) {
@@ -83,6 +87,27 @@ __global__ void gather_kernel(const char* __restrict__ kv, uint32_t rows_per_sli
         wait_vmcnt<D>();
         ++issued;
       }
+    }
+  } else if constexpr (MODE == 3 || MODE == 4) {
+    constexpr int R = MODE == 3 ? 4 : 2, L = 8 / R;   // rows and 128-byte lines per instruction
+    int issued = 0;
+    for (int grp = 0; grp < groups_per_wave; ++grp) {
+      for (int j = 0; j < 8; ++j) {
+        // rows (j % (8/R))·R .. +R of the group, lines (j / (8/R))·L .. +L
+        const int r = (j % (8 / R)) * R + lane % R, ch = (j / (8 / R)) * L * 8 + lane / R;
+        const uint32_t row = mix32((blockIdx.x * 4096u + w * 512u + grp) * 8u + r) % rows_per_slice;
+        __builtin_amdgcn_global_load_lds((const void*)(base + (uint64_t)row * row_bytes + ch * 16),
+                                         (__attribute__((address_space(3))) void*)(lds + ((w * 8 + (issued & 7)) & 63) * 1024),
+                                         16, 0, 0);
+        wait_vmcnt<D>();
+        ++issued;
+      }
+      const uint32_t row = mix32((blockIdx.x * 4096u + w * 512u + grp) * 8u + (lane & 7)) % rows_per_slice;
+      __builtin_amdgcn_global_load_lds((const void*)(base + (uint64_t)row * row_bytes + 1024 + ((lane >> 3) << 4)),
+                                       (__attribute__((address_space(3))) void*)(lds + ((w * 8 + (issued & 7)) & 63) * 1024),
+                                       16, 0, 0);
+      wait_vmcnt<D>();
+      ++issued;
     }
   } else if constexpr (MODE == 0) {
     int issued = 0;
@@ -167,6 +192,12 @@ int main() {
       run(gather_kernel<2, 8>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, rows", 8);
       run(gather_kernel<2, 32>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, rows", 32);
       run(gather_kernel<1, 16>, r, waves, 1024, 100 * 1024, gpw, "registers, lines", 16);
+      if (r.row_bytes == 1152 && waves <= 8) {
+        run(gather_kernel<3, 8>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, quads", 8);
+        run(gather_kernel<3, 32>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, quads", 32);
+        run(gather_kernel<4, 8>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, pairs", 8);
+        run(gather_kernel<4, 32>, r, waves, 1024, 100 * 1024, gpw, "direct-to-LDS, pairs", 32);
+      }
     }
     // two workgroups per CU (64 KB of LDS each)
     run(gather_kernel<0, 32>, r, 4, 2048, 64 * 1024, 64, "direct-to-LDS, lines", 32);
