@@ -265,9 +265,9 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
       });
     };
 
-    // ---- online softmax in steps on P = Σ_G scale·acc_G (as the fp8 pipelined
-    // kernel); step 5 publishes the block's S operands, one per V group G
-    // (bf16(S · scale_G(row))), and the rescale factors.
+    // ---- online softmax in steps on P = Σ_G scale·acc_G; step 5 publishes the
+    // block's S operands, one per V group G (bf16(S · scale_G(row))), and the
+    // rescale factors.
     struct Soft {
       float x[KT][4];
       float cur, alpha;
