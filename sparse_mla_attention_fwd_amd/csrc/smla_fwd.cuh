@@ -1165,7 +1165,17 @@ struct KvFp4Format {
 // past the last unit repeats its own previous unit (the same bytes to the
 // same LDS slot), so that every wave issues PER_WAVE instructions per block:
 // the waits count them.
-template <int NW, bool BUF, class Fmt>
+// SWZ: chunk c of row r sits at chunk c ^ swizzle(r) of the row's LDS span
+// (raw_swizzle below), so that reads of one chunk of eight consecutive rows
+// fall on distinct LDS banks; each row stays contiguous, so every instruction
+// still loads the same global bytes as without it.
+template <class Fmt>
+__device__ __forceinline__ int raw_swizzle(int row) {
+  // fp8: 640-byte rows, two rows apart share a bank offset -> XOR (r/2)%4;
+  // fp4: 320-byte rows, four rows apart do -> XOR (r/4)%2
+  return Fmt::ROW == 640 ? (row >> 1) & 3 : (row >> 2) & 1;
+}
+template <int NW, bool BUF, class Fmt, bool SWZ = false>
 struct RawGather {
   static constexpr int BT = 32;
   static constexpr int CHUNKS = Fmt::ROW / 16;                 // 16-byte chunks per row
@@ -1203,7 +1213,8 @@ struct RawGather {
     int u = k * NW + w;                                    // wave-uniform
     if (UNITS % NW != 0 && u >= UNITS) u -= NW;            // repeat this wave's previous unit
     const int c = u * 64 + l;
-    const int row = c / CHUNKS, ch = c - row * CHUNKS;
+    const int row = c / CHUNKS, pc = c - row * CHUNKS;
+    const int ch = SWZ ? pc ^ raw_swizzle<Fmt>(row) : pc;
     const int kvrow = dummy ? 0 : sidx_blk[row];
     if constexpr (BUF)
       src.load16((LDS_AS void*)(slot + u * 1024),

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
   constexpr int NR = FP4 ? 4 : 2;
   constexpr int NQ = 36;                      // QK MFMAs per block
   constexpr int NPV = 32;                     // PV MFMAs per block
-  using Gather = RawGather<NW, BUF, Fmt>;
+  using Gather = RawGather<NW, BUF, Fmt, true>;   // swizzled rows (conflict-free conversion reads)
   constexpr int LPB = Gather::PER_WAVE;       // gather instructions per wave per block
   constexpr int RAW = BT * Fmt::ROW;
   constexpr int TILE = BT * kRowBytesBf16;
@@ -121,10 +121,16 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
     static_assert(FP4 ? Fmt::CODE_BYTES == 288 : (Fmt::ROW == 640 && Fmt::CODE_BYTES == 576), "row formats");
     auto convert = [&](auto R, int p) __attribute__((always_inline)) {
       constexpr int r = decltype(R)::value;
-      const int row = 8 * w + (lane & 7), gsel = min(lane >> 3, 4);
+      const int row = 8 * w + (lane & 7), gsel = min(lane >> 3, 4), x = raw_swizzle<Fmt>(row);
       const uint32_t rbase = (uint32_t)(uintptr_t)(const LDS_AS void*)raws[r] + row * Fmt::ROW;
-      // 8 codes per chunk: 4 bytes (E2M1) or 8 bytes (E4M3)
-      const uint32_t caddr = rbase + (lane >> 3) * (FP4 ? 4 : 8), saddr = rbase + Fmt::CODE_BYTES + gsel * 4;
+      // 8 codes per bf16 chunk: 4 bytes (E2M1) or 8 bytes (E4M3).  Raw chunk
+      // (bf16 chunk 8k + l/8) / 4 or / 2 = 2k + l/32 (E2M1) or 4k + l/16
+      // (E4M3); the row's swizzle XORs its low bits, the k part rides in the
+      // immediate offsets.
+      const uint32_t caddr = FP4 ? rbase + ((((lane >> 5) ^ x) << 4) | (((lane >> 3) & 3) << 2))
+                                 : rbase + ((((lane >> 4) ^ x) << 4) | (((lane >> 3) & 1) << 3));
+      // scale g: byte 4(g%4) of raw chunk CODE_BYTES/16 + g/4 (low chunk bits free)
+      const uint32_t saddr = rbase + Fmt::CODE_BYTES + ((((gsel >> 2) ^ x) << 4) | ((gsel & 3) << 2));
       float scl;
       uint32_t o[9][4];
       if constexpr (FP4) {
