@@ -219,15 +219,16 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
     // 8G .. 8G+7 (group 4: 32..35).  Groups accumulate alternately in two
     // register sets; group G is folded (fp32 scale of the lane's key times its
     // partial sum) at the end of group G+1, group 3 after the last MFMA, and
-    // group 4 (set 0) by the softmax.  hook(i) runs after MFMA i.
+    // group 4 (set 0) by the softmax.  The scales of groups 0..3 stay in qo.sc
+    // for the S operands of the V groups.  hook(i) runs after MFMA i.
     struct QkOut {
       f32x4 acc[KT];          // group 4 partial sums
       float p[KT][4];         // groups 0..3, scaled
       float sc4g[KT][4];      // group 4 scales of this lane's keys
+      f32x4 sc[NW][KT];       // V-group scales (groups 0..3) of this lane's keys, for S
     };
     auto qk = [&](const char* tile, const float* stile, QkOut& qo, auto&& hook) __attribute__((always_inline)) {
       f32x4 acc[2][KT];
-      float scg[KT][4];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -240,11 +241,16 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
           for (int r = 0; r < 4; ++r) dst[kt][r] = v[r];
         }
       };
-      auto fold = [&](int set) __attribute__((always_inline)) {
+      auto fold = [&](int set, int G) __attribute__((always_inline)) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) qo.p[kt][r] = fmaf(scg[kt][r], acc[set][kt][r], qo.p[kt][r]);
+          for (int r = 0; r < 4; ++r) qo.p[kt][r] = fmaf(qo.sc[G][kt][r], acc[set][kt][r], qo.p[kt][r]);
+      };
+      auto read_vgroup_scales = [&](int G) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+          qo.sc[G][kt] = lds_load<f32x4>((const char*)stile, (G * BT + 16 * kt + 4 * g) * 4);
       };
       bf16x8 abuf[PF];
       static_for<0, PF>([&](auto I) __attribute__((always_inline)) {
@@ -258,10 +264,10 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
         acc[G & 1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             abuf[i % PF], qf[s], first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[G & 1][kt], 0, 0, 0);
         if constexpr (i + PF < NQ) abuf[i % PF] = lds_load<bf16x8>(tile, qk_off(i + PF));
-        if constexpr (i >= 8 && i % 8 == 0) read_group_scales(i / 8 - 1, scg);
-        if constexpr (i >= 15 && i % 8 == 7) fold(((i / 8) - 1) & 1);
+        if constexpr (i >= 8 && i % 8 == 0) read_vgroup_scales(i / 8 - 1);
+        if constexpr (i >= 15 && i % 8 == 7) fold(((i / 8) - 1) & 1, (i / 8) - 1);
         if constexpr (i == NQ - 1) {
-          fold(1);                            // group 3 (scales read after MFMA 32)
+          fold(1, 3);                         // group 3 (scales read after MFMA 32)
           read_group_scales(4, qo.sc4g);
           qo.acc[0] = acc[0][0];
           qo.acc[1] = acc[0][1];
@@ -335,24 +341,14 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
       }
     };
     constexpr int NSOFT = 6;
-    // V-group scales (groups 0..3) of this lane's keys 16kt + 4g + r: sc4[G][kt][r]
-    // (one 16-byte read per group and key tile: the tile is group-major)
-    auto read_scales = [&](const float* stile, f32x4 (&sc4)[NW][KT]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int G = 0; G < NW; ++G)
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) sc4[G][kt] = lds_load<f32x4>((const char*)stile, (G * BT + 16 * kt + 4 * g) * 4);
-    };
 
     // block 0: QKᵀ and softmax, published for iteration 0
     {
       QkOut qo;
       qk(tiles[0], stiles[0], qo, [&](auto) {});
-      f32x4 sc4[NW][KT];
-      read_scales(stiles[0], sc4);
       Soft sm;
       static_for<0, NSOFT>([&](auto K) __attribute__((always_inline)) {
-        soft_step(K, sm, qo, 4 * g, sc4, 0);
+        soft_step(K, sm, qo, 4 * g, qo.sc, 0);
       });
     }
 
@@ -395,7 +391,6 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
       };
 
       QkOut qo;
-      f32x4 sc4[NW][KT];
       if (next) {
         qk(tiles[p ^ 1], stiles[p ^ 1], qo, [&](auto I) __attribute__((always_inline)) {
           constexpr int q = decltype(I)::value;
@@ -404,7 +399,6 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
             fetch_v((q - (NQ - PF)) / 2);
           dma_at(I);
         });
-        read_scales(stiles[p ^ 1], sc4);
       } else {
         consume_reads();
 #pragma unroll
@@ -439,7 +433,7 @@ __global__ __launch_bounds__(256) void smla_fwd_q_pipe_kernel(FwdArgs a) {
         st.o[ht * 8 + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.v, sop[ht], st.o[ht * 8 + jj], 0, 0, 0);
         if constexpr (ht == NW - 1 && jj + PFV < 8) fetch_v(jj + PFV);
         if constexpr (c % 4 == 1 && c / 4 < NSOFT) {
-          if (next) soft_step(std::integral_constant<int, c / 4>{}, sm, qo, j1, sc4, p ^ 1);
+          if (next) soft_step(std::integral_constant<int, c / 4>{}, sm, qo, j1, qo.sc, p ^ 1);
         }
         dma_at(std::integral_constant<int, NQ + c>{});
         __builtin_amdgcn_sched_barrier(0);
