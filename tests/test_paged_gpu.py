@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import workloads
-from oracle import dequant_fp8_rows
+from oracle import dequant_fp4_rows, dequant_fp8_rows
 from oracle.paged import sparse_mla_fwd_paged
 from test_parity_gpu import check
 
@@ -95,6 +95,27 @@ def test_paged_fp8_cases(dev, num_splits):
     out, lse = run_paged(dev, x, num_splits=num_splits)
     ro, rl = oracle_paged(x)
     check(out, lse, ro, rl, f"paged fp8 ns={num_splits}")
+
+
+@pytest.mark.parametrize("h_q,num_splits", [(64, 0), (64, 2), (32, 1), (128, 4)])
+def test_paged_fp4_cases(dev, h_q, num_splits):
+    """An fp4 (E2M1) page pool through the block table: the translated rows
+    feed the fp4 kernels (64-head pipelined, 16/32-head cooperative) unchanged."""
+    x = workloads.make_random_paged(s_q=4, h_q=h_q, topk=700, page_size=16, num_pages=70,
+                                    table_width=64, seed=88 + h_q + num_splits, unallocated_frac=0.15,
+                                    invalid_frac=0.1, kv_format="fp4")
+    device, smla = dev
+    kv = smla.pack_fp4_kv(x["kv_codes"], x["kv_scales"], device)
+    out, lse = smla.sparse_mla_fwd(x["q"].to(device), kv, x["indices"].to(device), x["sm_scale"],
+                                   kv_format="fp4", block_table=x["block_table"].to(device),
+                                   page_size=x["page_size"], num_splits=num_splits)
+    torch.cuda.synchronize()
+    # the oracle on the whole (small) dequantised pool
+    kv_pages = dequant_fp4_rows(x["kv_codes"].numpy(), x["kv_scales"].numpy()).reshape(-1, 16, 576)
+    ro, rl = sparse_mla_fwd_paged(workloads.to_f64(x["q"]), kv_pages, x["block_table"].numpy().astype(np.int64),
+                                  x["indices"].numpy(), x["sm_scale"], 512)
+    check(out.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64), ro, rl,
+          f"paged fp4 h{h_q} ns={num_splits}")
 
 
 def test_identity_table_is_bit_identical_to_flat_kv(dev):
