@@ -312,6 +312,23 @@ def test_fp8_long_split_cases(dev, h_q, topk, num_splits):
     assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
 
 
+@pytest.mark.parametrize("h_q,topk,num_splits", [(64, 1500, 1), (64, 2048, 2), (128, 2048, 3)])
+def test_fp8_pipelined_frequent_rescales(dev, h_q, topk, num_splits):
+    """The 64-head fp8 kernel with Q x 8: the running max moves in most blocks,
+    so the per-head-tile rescale of the accumulators runs often, also after
+    leading blocks that are fully masked (token 1) and between valid blocks
+    separated by masked ones (token 2)."""
+    x = workloads.make_random(s_q=5, h_q=h_q, topk=topk, s_kv=6000, seed=300 + h_q + num_splits,
+                              kv_format="fp8", invalid_frac=0.1, q_mult=8.0)
+    idx = x["indices"]
+    idx[1, :700] = -1
+    idx[2, 100:900] = -1
+    idx[2, 1200:1800] = -1
+    out, lse = run_gpu(dev, x, num_splits=num_splits)
+    ro, rl = oracle_tokens(x)
+    check(out, lse, ro, rl, f"fp8 Qx8 h{h_q} splits={num_splits}")
+
+
 def test_fp8_single_row_matches_dequant(dev):
     """All slots on one row: out is that row's V = code * scale.  The codes are
     used exactly and the scale enters through the bf16 S operand, so each
