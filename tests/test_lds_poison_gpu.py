@@ -10,6 +10,10 @@ results instead of a plausible stale value.  (Page "FlashMLAÁÆóÂ≠êAscend 950ÁßªÊ
 to the synchronisation between loads and compute; this build makes a missing
 wait or barrier visible.)
 
+All cases keep the KV inside the 32-bit buffer window: there a poisoned index
+(-1) that a racing gather used as a row would become an out-of-window offset,
+which the hardware drops, instead of an address below the KV.
+
 Each case runs the product library and the debug library on the same inputs.
 The debug run must be finite, bit-identical to the product run (the poison
 writes add waits, never arithmetic) and within the parity bar of the oracle.
